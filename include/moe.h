@@ -1,0 +1,164 @@
+/*
+ * moe.h — C ABI of one rank's MoE expert-layer forward on an AMD Instinct
+ * MI355X (gfx950): router top-k, token dispatch, grouped expert GEMM with
+ * SwiGLU, and the weighted combine.
+ *
+ * Sources of the operations (page title, then section):
+ *   [EP] "Paralelismo de especialistas" (transformers v5.23.0 docs, pt), with
+ *        the tr ("Uzman paralelliği") and zh ("专家并行") pages of transformers main;
+ *   [TP] "Paralelismo de tensor para inferência" (transformers main docs, pt).
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer to a dense row-major array that
+ *     the caller allocates and owns. The library allocates nothing and keeps no
+ *     global mutable state; calls on different streams may run concurrently
+ *     when they write disjoint buffers.
+ *   - Every call validates its arguments on the host, enqueues its kernels on
+ *     `stream` and returns without synchronising. Invalid arguments return
+ *     MOE_EINVAL (or MOE_EUNSUPPORTED for a valid but unsupported shape) before
+ *     anything is enqueued, so no output is touched on error. A failed kernel
+ *     launch returns MOE_EHIP. Faults inside kernels surface at the caller's
+ *     next synchronisation.
+ *   - Shapes: T tokens on this rank (T = 0 is a valid no-op call), hidden size
+ *     d, expert FFN width d_ff, E global experts, top-k k, and this rank's
+ *     contiguous block of local experts [e_begin, e_end) with
+ *     E_loc = e_end - e_begin. A flat pair index is p = t*k + j.
+ *     N_max = T * min(k, E_loc) bounds the number of local pairs N_loc, so every
+ *     buffer can be sized on the host without reading any device value (the
+ *     layer needs no host synchronisation).
+ *   - Limits: 1 <= k <= E <= 1024; T*k < 2^31; d and d_ff are multiples of 8
+ *     (16-byte rows of bf16); 1 <= E_loc.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,       /* invalid argument (null pointer, bad shape, bad range) */
+  MOE_EUNSUPPORTED = 2, /* valid but unsupported (e.g. E > 1024) */
+  MOE_EHIP = 3          /* a HIP launch failed */
+} moe_status;
+
+/* Element type of activations, weights, H, Y and outputs. Router logits and
+ * routing weights are always fp32; indices are always int32. */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef struct {
+  int64_t T;        /* tokens in this call, >= 0 */
+  int32_t d;        /* hidden size, > 0, multiple of 8 */
+  int32_t d_ff;     /* expert FFN width, > 0, multiple of 8 */
+  int32_t E;        /* global experts */
+  int32_t k;        /* experts per token, 1 <= k <= E */
+  int32_t e_begin;  /* first local expert (global id) */
+  int32_t e_end;    /* one past the last local expert; 0 <= e_begin < e_end <= E */
+} moe_shape;
+
+/* Human-readable name of a status code (static storage). */
+const char* moe_status_string(moe_status status);
+
+/* Local expert block of `rank` under expert parallelism of size `ep`:
+ * [EP] "Como os tamanhos se combinam": ep_size cuts the expert list into
+ * ep_size contiguous blocks, each rank computes E/ep experts and ep_size
+ * consecutive ranks hold a full set, so the block of rank r is
+ * [(r % ep) * E/ep, (r % ep + 1) * E/ep). Host-only; writes *e_begin, *e_end.
+ * MOE_EINVAL unless E >= 1, ep >= 1, E % ep == 0, rank >= 0 and both output
+ * pointers are non-null. */
+moe_status moe_expert_range(int32_t E, int32_t ep, int32_t rank,
+                            int32_t* e_begin, int32_t* e_end);
+
+/* Router top-k ([EP] "Adicionando uma implementação": the implementation is
+ * called with top_k_index / top_k_weights; [EP] intro: each token activates
+ * only a few experts).
+ *   logits   [T, E] fp32, read only.
+ *   topk_idx [T, k] int32, written: the k largest logits of each token in
+ *            descending order; equal logits go to the lower expert id and
+ *            -0.0 equals +0.0. Global expert ids.
+ *   topk_w   [T, k] fp32, written: softmax over the k selected logits (they
+ *            sum to 1 per token), computed in fp32.
+ * Logits must be finite; NaN/Inf give unspecified ids but never a fault.
+ * Uses s->T, s->E, s->k only. */
+moe_status moe_route_topk(const moe_shape* s, const float* logits,
+                          int32_t* topk_idx, float* topk_w, hipStream_t stream);
+
+/* Bytes of device workspace moe_dispatch needs for this shape (may be 0). */
+size_t moe_dispatch_workspace_bytes(const moe_shape* s);
+
+/* Token dispatch on one rank ([EP] "Despacho de tokens": every (token, expert)
+ * pair goes to the rank owning the expert and only local experts compute;
+ * [EP] "Como os tamanhos se combinam": ownership is one contiguous block, so
+ * this rank's pairs form one contiguous segment of the expert-sorted list;
+ * [TP] EpRouterParallel row: local experts are addressed by local ids).
+ *   x        [T, d] dt, read only: hidden states.
+ *   topk_idx [T, k] int32, read only: global expert ids. An id outside [0, E)
+ *            is dropped: not counted, pair_pos = -1, and the perm slots it
+ *            would take (past offsets[E]) are left unwritten.
+ *   counts   [E]   int32, written: pairs per expert over ALL experts.
+ *   offsets  [E+1] int32, written: exclusive prefix sum of counts.
+ *   perm     [T*k] int32, written: sorted slot -> flat pair p, pairs sorted by
+ *            expert id, stable in p inside each expert.
+ *   pair_pos [T*k] int32, written: flat pair -> row in x_perm of this rank
+ *            (slot - offsets[e_begin]) for a local pair, -1 otherwise.
+ *   x_perm   [N_max, d] dt, written: rows [0, N_loc) hold x[perm[offsets
+ *            [e_begin] + r] / k]; rows past N_loc are left unwritten.
+ *   workspace moe_dispatch_workspace_bytes(s) bytes of device memory (may be
+ *            NULL when that is 0); contents on entry do not matter.
+ * T = 0 still writes counts and offsets (all zero). */
+moe_status moe_dispatch(const moe_shape* s, moe_dtype dt, const void* x,
+                        const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                        int32_t* perm, int32_t* pair_pos, void* x_perm,
+                        void* workspace, hipStream_t stream);
+
+/* Bytes of device workspace moe_grouped_gemm needs for this shape (may be 0). */
+size_t moe_grouped_gemm_workspace_bytes(const moe_shape* s, moe_dtype dt);
+
+/* Grouped expert FFN over this rank's local experts: experts_forward of
+ * [EP] "Adicionando uma implementação", with the weights sharded along the
+ * expert dimension ([EP] GroupedGemmParallel) and the packed gate/up layout of
+ * [TP] "Estratégias empacotadas" (gate = first d_ff columns, up = the rest).
+ * For each local expert e with rows R (its segment of x_perm):
+ *     H_R = silu(R @ Wgu[e][:, :d_ff]) * (R @ Wgu[e][:, d_ff:])
+ *     Y_R = H_R @ Wdn[e]
+ * with fp32 accumulation; for dt = MOE_BF16, H and Y are rounded to bf16 (RNE).
+ *   x_perm    [N_max, d] dt, read only (rows [0, N_loc) are used).
+ *   offsets   [E+1] int32 DEVICE array from moe_dispatch; the row counts are
+ *             read on the device, never on the host.
+ *   w_gate_up [E_loc, d, 2*d_ff] dt, read only. Empty experts are not read.
+ *   w_down    [E_loc, d_ff, d] dt, read only.
+ *   h         [N_max, d_ff] dt, written (intermediate activations).
+ *   y         [N_max, d] dt, written: rows [0, N_loc).
+ *   workspace moe_grouped_gemm_workspace_bytes(s, dt) bytes (may be NULL if 0).
+ * Uses s->T, d, d_ff, k, e_begin, e_end. */
+moe_status moe_grouped_gemm(const moe_shape* s, moe_dtype dt, const void* x_perm,
+                            const int32_t* offsets, const void* w_gate_up,
+                            const void* w_down, void* h, void* y, void* workspace,
+                            hipStream_t stream);
+
+/* Weighted combine back to token order ([EP] "Despacho de tokens": results are
+ * combined with the routing weights; "Adicionando uma implementação": the
+ * output is the weighted expert output of every token this rank holds):
+ *     out[t] = sum over j = 0..k-1 with pair_pos[t*k+j] >= 0 of
+ *              topk_w[t, j] * y[pair_pos[t*k+j]]
+ * accumulated in fp32 in slot order, rounded once to dt. A token with no local
+ * pair gets a zero row; every one of the T rows is written.
+ *   y        [N_max, d] dt, read only.
+ *   pair_pos [T*k] int32, read only (values must be -1 or < N_max).
+ *   topk_w   [T, k] fp32, read only.
+ *   out      [T, d] dt, written. */
+moe_status moe_combine(const moe_shape* s, moe_dtype dt, const void* y,
+                       const int32_t* pair_pos, const float* topk_w, void* out,
+                       hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -8,6 +8,7 @@ from .moe import (  # noqa: F401
     route_topk,
     dispatch,
     silu,
+    swiglu_hidden,
     expert_ffn,
     grouped_experts,
     combine,

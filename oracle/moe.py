@@ -121,6 +121,18 @@ def silu(z: np.ndarray) -> np.ndarray:
     return out
 
 
+def swiglu_hidden(rows: np.ndarray, w_gate_up: np.ndarray) -> np.ndarray:
+    """H = silu(gate) * up for one expert's rows, gate/up from the packed weight.
+
+    [TP] "Estratégias empacotadas": gate_up = x @ gate_up_proj, then
+    chunk(2, dim=-1) gives gate (first half of the columns) and up (second half).
+    """
+    w_gate_up = np.asarray(w_gate_up, dtype=np.float64)
+    d_ff = w_gate_up.shape[1] // 2
+    g = np.asarray(rows, dtype=np.float64) @ w_gate_up
+    return silu(g[:, :d_ff]) * g[:, d_ff:]
+
+
 def expert_ffn(rows: np.ndarray, w_gate_up: np.ndarray, w_down: np.ndarray) -> np.ndarray:
     """One expert's SwiGLU FFN on its rows.
 
@@ -130,11 +142,7 @@ def expert_ffn(rows: np.ndarray, w_gate_up: np.ndarray, w_down: np.ndarray) -> n
     silu(gate) * up; the down projection [d_ff, d] follows ([EP] plan entry
     "mlp.experts.down_proj" with rule "grouped_gemm").
     """
-    rows = np.asarray(rows, dtype=np.float64)
-    d_ff = w_down.shape[0]
-    g = rows @ np.asarray(w_gate_up, dtype=np.float64)
-    h = silu(g[:, :d_ff]) * g[:, d_ff:]
-    return h @ np.asarray(w_down, dtype=np.float64)
+    return swiglu_hidden(rows, w_gate_up) @ np.asarray(w_down, dtype=np.float64)
 
 
 def grouped_experts(x_perm: np.ndarray, offsets: np.ndarray, e_lo: int, e_hi: int,

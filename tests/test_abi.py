@@ -1,0 +1,125 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol, and
+rejects invalid arguments on the host before any HIP call."""
+import ctypes
+import os
+
+import pytest
+
+import token_dispatch_grouped_amd as moe
+
+pytestmark = pytest.mark.skipif(not os.path.exists(moe.lib_path), reason="libmoe.so not built")
+
+NULL = ctypes.c_void_p(0)
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def test_exports_every_declared_symbol():
+    declared = moe.declared_symbols()
+    assert set(declared) >= {"moe_route_topk", "moe_dispatch", "moe_grouped_gemm", "moe_combine",
+                             "moe_expert_range", "moe_status_string"}
+    lib = moe.lib()
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in (0, 1, 2, 3):
+        assert moe.status_string(code).startswith("MOE_")
+
+
+def test_expert_range_matches_ownership_diagram():
+    golden = os.path.join(os.path.dirname(__file__), "golden", "ep_ownership_8ranks.txt")
+    with open(golden) as f:
+        rows = [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+    for row in rows:
+        ep = int(row[0])
+        for rank, spec in enumerate(row[1:]):
+            lo, hi = (int(v) for v in spec.split("-"))
+            assert moe.expert_range(8, ep, rank) == (lo, hi + 1)
+    with pytest.raises(moe.MoeError):
+        moe.expert_range(8, 3, 0)
+    with pytest.raises(moe.MoeError):
+        moe.expert_range(8, 2, -1)
+
+
+def _shape(**kw):
+    base = dict(T=16, d=64, d_ff=64, E=8, k=2, e_begin=0, e_end=8)
+    base.update(kw)
+    return moe.shape(**base)
+
+
+def _route(s, logits=FAKE, idx=FAKE, w=FAKE):
+    return moe.lib().moe_route_topk(ctypes.byref(s), logits, idx, w, NULL)
+
+
+def _dispatch(s, dt=moe.MOE_BF16, ptrs=None):
+    p = ptrs or [FAKE] * 7
+    return moe.lib().moe_dispatch(ctypes.byref(s), dt, p[0], p[1], p[2], p[3], p[4], p[5], p[6], FAKE, NULL)
+
+
+def _gemm(s, dt=moe.MOE_BF16, ptrs=None):
+    p = ptrs or [FAKE] * 6
+    return moe.lib().moe_grouped_gemm(ctypes.byref(s), dt, p[0], p[1], p[2], p[3], p[4], p[5], NULL, NULL)
+
+
+def _combine(s, dt=moe.MOE_BF16, ptrs=None):
+    p = ptrs or [FAKE] * 4
+    return moe.lib().moe_combine(ctypes.byref(s), dt, p[0], p[1], p[2], p[3], NULL)
+
+
+@pytest.mark.parametrize("kw", [dict(k=0), dict(k=9), dict(E=0), dict(T=-1), dict(T=2**30, k=4)])
+def test_route_rejects_bad_shapes(kw):
+    assert _route(_shape(**kw)) == moe.MOE_EINVAL
+
+
+def test_route_rejects_null_and_large_E():
+    assert _route(_shape(), logits=NULL) == moe.MOE_EINVAL
+    assert _route(_shape(), idx=NULL) == moe.MOE_EINVAL
+    assert _route(_shape(E=2048, k=2)) == moe.MOE_EUNSUPPORTED
+    assert moe.lib().moe_route_topk(None, FAKE, FAKE, FAKE, NULL) == moe.MOE_EINVAL
+
+
+@pytest.mark.parametrize("kw", [dict(d=12), dict(d_ff=20), dict(d=0), dict(e_begin=4, e_end=4),
+                                dict(e_begin=-1), dict(e_end=9), dict(k=0)])
+def test_layer_steps_reject_bad_shapes(kw):
+    s = _shape(**kw)
+    assert _dispatch(s) == moe.MOE_EINVAL
+    assert _gemm(s) == moe.MOE_EINVAL
+    assert _combine(s) == moe.MOE_EINVAL
+
+
+def test_layer_steps_reject_null_and_bad_dtype():
+    s = _shape()
+    for i in range(7):
+        p = [FAKE] * 7
+        p[i] = NULL
+        assert _dispatch(s, ptrs=p) == moe.MOE_EINVAL, i
+    for i in range(6):
+        p = [FAKE] * 6
+        p[i] = NULL
+        assert _gemm(s, ptrs=p) == moe.MOE_EINVAL, i
+    for i in range(4):
+        p = [FAKE] * 4
+        p[i] = NULL
+        assert _combine(s, ptrs=p) == moe.MOE_EINVAL, i
+    assert _dispatch(s, dt=7) == moe.MOE_EINVAL
+    assert _gemm(s, dt=7) == moe.MOE_EINVAL
+    assert _combine(s, dt=7) == moe.MOE_EINVAL
+
+
+def test_workspace_sizes():
+    lib = moe.lib()
+    s = _shape(T=0)
+    assert lib.moe_dispatch_workspace_bytes(ctypes.byref(s)) == 0
+    s = _shape(T=16384, k=8, E=256)
+    # one int32 per (expert, chunk of 1024 pairs)
+    assert lib.moe_dispatch_workspace_bytes(ctypes.byref(s)) == 256 * 128 * 4
+    assert lib.moe_grouped_gemm_workspace_bytes(ctypes.byref(s), moe.MOE_BF16) == 0
+
+
+def test_zero_tokens_is_a_no_op_on_the_host():
+    s = _shape(T=0)
+    # T = 0: nothing is enqueued for route, gemm and combine, so null tensors are fine
+    assert _route(s, logits=NULL, idx=NULL, w=NULL) == moe.MOE_OK
+    assert _gemm(s, ptrs=[NULL] * 6) == moe.MOE_OK
+    assert _combine(s, ptrs=[NULL] * 4) == moe.MOE_OK

@@ -1,0 +1,226 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Indices (top-k ids, counts, offsets, permutation, pair positions) and gathered
+rows are compared bit for bit; floating results within max|err|/max|ref| of
+2e-2 (bf16) or 1e-5 (fp32), routing weights within 1e-6 absolute.
+"""
+import numpy as np
+import pytest
+
+import moe_inputs as mi
+import oracle
+from tests import _gpu as g
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - collected on CPU hosts too
+    pytest.skip("no GPU", allow_module_level=True)
+
+import token_dispatch_grouped_amd as moe  # noqa: E402
+
+
+def _layer_case(w: mi.Workload, logits=None):
+    """Run the layer on the device and the oracle on the host; compare everything."""
+    if logits is None:
+        logits = mi.router_logits(w)
+    x = mi.hidden_states(w)
+    wgu, wdn = mi.expert_weights(w)
+    print(f"case {w}", flush=True)
+    res = moe.layer(g.to_dev(x, w.dtype), g.to_dev(logits, "f32"), g.to_dev(wgu, w.dtype),
+                    g.to_dev(wdn, w.dtype), w.k, w.e_begin, w.e_end)
+    torch.cuda.synchronize()
+    x64, wgu64, wdn64 = mi.to_f64(x, w.dtype), mi.to_f64(wgu, w.dtype), mi.to_f64(wdn, w.dtype)
+    ref = oracle.moe_layer(x64, logits, w.k, w.e_begin, w.e_end, wgu64, wdn64)
+    np.testing.assert_array_equal(res["idx"].cpu().numpy(), ref["idx"])
+    np.testing.assert_allclose(res["w"].cpu().numpy(), ref["w"], rtol=0, atol=g.W_ATOL)
+    np.testing.assert_array_equal(res["counts"].cpu().numpy(), ref["counts"])
+    np.testing.assert_array_equal(res["offsets"].cpu().numpy(), ref["offsets"])
+    np.testing.assert_array_equal(res["perm"].cpu().numpy(), ref["perm"])
+    np.testing.assert_array_equal(res["pair_pos"].cpu().numpy(), ref["pair_pos"])
+    n_loc = ref["x_perm"].shape[0]
+    np.testing.assert_array_equal(g.to_f64(res["x_perm"][:n_loc]), ref["x_perm"])
+    # H against the oracle's H on the same rows
+    offs = ref["offsets"]
+    base = offs[w.e_begin]
+    h_gpu = g.to_f64(res["h"][:n_loc])
+    h_ref = np.zeros_like(h_gpu)
+    for e in range(w.e_begin, w.e_end):
+        r0, r1 = offs[e] - base, offs[e + 1] - base
+        if r1 > r0:
+            h_ref[r0:r1] = oracle.swiglu_hidden(ref["x_perm"][r0:r1], wgu64[e - w.e_begin])
+    tol = g.TOL[w.dtype]
+    assert g.rel_err(h_gpu, h_ref) <= tol
+    assert g.rel_err(g.to_f64(res["y"][:n_loc]), ref["y"]) <= tol
+    err = g.rel_err(g.to_f64(res["out"]), ref["out"])
+    print(f"  out max|err|/max|ref| = {err:.3e}", flush=True)
+    assert err <= tol
+    return res, ref
+
+
+# ----------------------------------------------------------------------------- route top-k
+
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (7, 2, 2), (33, 3, 2), (257, 8, 2), (129, 8, 8), (100, 100, 7),
+                                   (300, 128, 4), (65, 256, 8), (10, 1024, 3), (3, 1024, 1024), (0, 16, 4)])
+def test_route_topk_matches_oracle(T, E, k):
+    rng = np.random.default_rng(T * 1000 + E * 10 + k)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    idx, w = moe.route_topk(g.to_dev(logits, "f32"), k)
+    ref_idx, ref_w = oracle.route_topk(logits, k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx)
+    np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=0, atol=g.W_ATOL)
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (128, 4), (256, 8), (40, 40)])
+def test_route_topk_ties_and_signed_zeros(E, k):
+    rng = np.random.default_rng(E + k)
+    T = 500
+    logits = (rng.integers(-2, 3, size=(T, E)) * 0.5).astype(np.float32)  # many exact ties
+    logits[rng.random((T, E)) < 0.2] = -0.0
+    logits[rng.random((T, E)) < 0.1] = 0.0
+    logits[0] = 0.0  # an all-equal row: ids 0..k-1
+    idx, w = moe.route_topk(g.to_dev(logits, "f32"), k)
+    ref_idx, ref_w = oracle.route_topk(logits, k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx)
+    np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=0, atol=g.W_ATOL)
+    np.testing.assert_array_equal(idx.cpu().numpy()[0], np.arange(k))
+
+
+# ----------------------------------------------------------------------------- dispatch
+
+@pytest.mark.parametrize("T,E,k,lo,hi", [(1, 8, 2, 0, 8), (1000, 8, 2, 0, 8), (1500, 32, 4, 8, 12),
+                                         (3000, 256, 8, 0, 32), (2047, 1024, 4, 1000, 1024),
+                                         (5, 128, 4, 0, 128), (1025, 16, 16, 3, 4)])
+def test_dispatch_matches_oracle(T, E, k, lo, hi):
+    rng = np.random.default_rng(T + E + k)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[:, lo] += 2.0  # one heavy local expert
+    d = 72
+    x = mi.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    idx_np, _ = oracle.route_topk(logits, k)
+    idx = torch.from_numpy(idx_np.astype(np.int32)).cuda()
+    disp = moe.dispatch(g.to_dev(x, "bf16"), idx, E, lo, hi)
+    torch.cuda.synchronize()
+    counts, offsets, perm, pair_pos, x_perm = oracle.dispatch(idx_np, E, lo, hi, mi.to_f64(x, "bf16"))
+    np.testing.assert_array_equal(disp.counts.cpu().numpy(), counts)
+    np.testing.assert_array_equal(disp.offsets.cpu().numpy(), offsets)
+    np.testing.assert_array_equal(disp.perm.cpu().numpy(), perm)
+    np.testing.assert_array_equal(disp.pair_pos.cpu().numpy(), pair_pos)
+    np.testing.assert_array_equal(g.to_f64(disp.x_perm[: x_perm.shape[0]]), x_perm)
+
+
+def test_dispatch_zero_tokens_writes_zero_counts():
+    E = 16
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty((0, 2), dtype=torch.int32, device="cuda")
+    disp = moe.dispatch_alloc(x, 2, E, 0, 8)
+    disp.counts.fill_(7)
+    disp.offsets.fill_(7)
+    moe.dispatch(x, idx, E, 0, 8, out=disp)
+    torch.cuda.synchronize()
+    assert disp.counts.cpu().tolist() == [0] * E
+    assert disp.offsets.cpu().tolist() == [0] * (E + 1)
+
+
+def test_dispatch_drops_out_of_range_ids():
+    T, E, k, d = 300, 8, 2, 64
+    rng = np.random.default_rng(5)
+    idx_np = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    bad = rng.random((T, k)) < 0.1
+    idx_np[bad] = np.where(rng.random(bad.sum()) < 0.5, -1, E + 3)
+    x = mi.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    disp = moe.dispatch(g.to_dev(x, "bf16"), torch.from_numpy(idx_np).cuda(), E, 0, E)
+    torch.cuda.synchronize()
+    good = idx_np.reshape(-1)[~bad.reshape(-1)]
+    np.testing.assert_array_equal(disp.counts.cpu().numpy(), np.bincount(good, minlength=E))
+    pp = disp.pair_pos.cpu().numpy()
+    assert np.all(pp[bad.reshape(-1)] == -1)
+    assert sorted(pp[~bad.reshape(-1)].tolist()) == list(range(good.size))
+
+
+# ----------------------------------------------------------------------------- whole layer, small
+
+SMALL = [
+    mi.WORKLOADS["tiny_fp32"],  # the full tiny fp32 workload
+    mi.Workload("dense8_small", 1200, 328, 200, 8, 2, 0, 8, "bf16", 11),          # K tails, ragged N, 2 row tiles
+    mi.Workload("ep_share_small", 900, 256, 264, 32, 4, 8, 12, "bf16", 12),       # 4 of 32 experts local
+    mi.Workload("skew_small", 1000, 320, 128, 64, 8, 0, 16, "bf16", 13, 1.5),    # skewed, empty experts
+    mi.Workload("decode_small", 5, 256, 192, 128, 4, 0, 128, "bf16", 14),        # mostly empty experts
+    mi.Workload("single_token", 1, 64, 64, 8, 2, 0, 8, "bf16", 15),
+    mi.Workload("one_local_expert", 700, 128, 136, 8, 3, 5, 6, "bf16", 16),
+    mi.Workload("fp32_ragged", 200, 72, 40, 6, 2, 1, 5, "f32", 17),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_layer_matches_oracle(w):
+    _layer_case(w)
+
+
+def test_layer_all_tokens_on_one_expert():
+    w = mi.Workload("one_hot", 700, 192, 256, 16, 1, 0, 16, "bf16", 18)
+    logits = mi.router_logits(w)
+    logits[:, 9] += 100.0  # every token's top-1 is expert 9: 700 rows, 3 row tiles
+    res, ref = _layer_case(w, logits)
+    assert int(ref["counts"][9]) == 700
+
+
+def test_layer_zero_tokens():
+    w = mi.Workload("empty", 0, 64, 64, 8, 2, 0, 8, "bf16", 19)
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    logits = torch.empty((0, 8), dtype=torch.float32, device="cuda")
+    wgu = torch.zeros((8, 64, 128), dtype=torch.bfloat16, device="cuda")
+    wdn = torch.zeros((8, 64, 64), dtype=torch.bfloat16, device="cuda")
+    res = moe.layer(x, logits, wgu, wdn, w.k, 0, 8)
+    torch.cuda.synchronize()
+    assert res["out"].shape == (0, 64)
+    assert res["counts"].cpu().tolist() == [0] * 8
+
+
+def test_rank_sum_on_one_gpu():
+    """Masked partial outputs of every rank's share add up to the full layer."""
+    base = mi.Workload("rank_sum", 512, 192, 128, 16, 4, 0, 16, "bf16", 20)
+    logits = g.to_dev(mi.router_logits(base), "f32")
+    x = g.to_dev(mi.hidden_states(base), "bf16")
+    wgu_np, wdn_np = mi.expert_weights(base)
+    wgu, wdn = g.to_dev(wgu_np, "bf16"), g.to_dev(wdn_np, "bf16")
+    full = moe.layer(x, logits, wgu, wdn, base.k, 0, 16)["out"].float()
+    for ep in (2, 4, 8):
+        acc = torch.zeros_like(full)
+        for r in range(ep):
+            lo, hi = moe.expert_range(16, ep, r)
+            acc += moe.layer(x, logits, wgu[lo:hi].contiguous(), wdn[lo:hi].contiguous(), base.k, lo, hi)["out"].float()
+        torch.cuda.synchronize()
+        err = g.rel_err(acc.cpu().numpy().astype(np.float64), full.cpu().numpy().astype(np.float64))
+        assert err <= 2e-2, (ep, err)
+
+
+def test_identity_expert_round_trip():
+    """dispatch then combine with y = x_perm (an identity expert) gives back x."""
+    T, E, k, d = 777, 8, 3, 136
+    rng = np.random.default_rng(21)
+    x_np = mi.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    x = g.to_dev(x_np, "bf16")
+    idx, w = moe.route_topk(g.to_dev(rng.standard_normal((T, E)).astype(np.float32), "f32"), k)
+    disp = moe.dispatch(x, idx, E, 0, E)
+    out = moe.combine(disp.x_perm, disp.pair_pos, w, T, k, E, 0, E)
+    torch.cuda.synchronize()
+    # sum_j w_j = 1 in fp32: out equals x up to one bf16 rounding
+    assert g.rel_err(g.to_f64(out), mi.to_f64(x_np, "bf16")) <= 2 ** -8
+
+
+def test_layer_is_deterministic():
+    w = mi.Workload("determinism", 1500, 256, 192, 32, 4, 0, 32, "bf16", 22)
+    args = (g.to_dev(mi.hidden_states(w), "bf16"), g.to_dev(mi.router_logits(w), "f32"),
+            *(g.to_dev(a, "bf16") for a in mi.expert_weights(w)))
+    a = moe.layer(*args, w.k, w.e_begin, w.e_end)
+    b = moe.layer(*args, w.k, w.e_begin, w.e_end)
+    torch.cuda.synchronize()
+    n_loc = int(a["offsets"][w.e_end] - a["offsets"][w.e_begin])
+    for key in ("perm", "pair_pos", "out", "h", "y"):
+        ta, tb = a[key], b[key]
+        if key in ("h", "y"):
+            ta, tb = ta[:n_loc], tb[:n_loc]
+        if ta.dtype == torch.bfloat16:
+            ta, tb = ta.view(torch.int16), tb.view(torch.int16)
+        assert torch.equal(ta, tb), key

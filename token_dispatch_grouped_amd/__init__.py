@@ -1,0 +1,255 @@
+"""MI355X (gfx950) MoE expert-layer forward on one rank's share: Python binding.
+
+Thin ctypes marshalling over libmoe.so (include/moe.h). Every step of the path
+runs in the library's HIP kernels; PyTorch only provides device memory and the
+current stream. There is no fallback: if the library is missing, importing the
+binding works only for introspection (`lib_path`, `declared_symbols`) and every
+compute call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_ROOT = os.path.dirname(_PKG)
+lib_path = os.path.join(_PKG, "libmoe.so")
+header_path = os.path.join(_ROOT, "include", "moe.h")
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP = 0, 1, 2, 3
+MOE_F32, MOE_BF16 = 0, 1
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class moe_shape(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int64),
+        ("d", ctypes.c_int32),
+        ("d_ff", ctypes.c_int32),
+        ("E", ctypes.c_int32),
+        ("k", ctypes.c_int32),
+        ("e_begin", ctypes.c_int32),
+        ("e_end", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise ImportError(
+                f"{lib_path} is missing: build it with token_dispatch_grouped_amd.build.build() "
+                "(there is no fallback path)")
+        lib = ctypes.CDLL(lib_path)
+        P, S, I32, I64, SZ = ctypes.c_void_p, ctypes.POINTER(moe_shape), ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        sigs = {
+            "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+            "moe_expert_range": (ctypes.c_int, [I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
+            "moe_route_topk": (ctypes.c_int, [S, P, P, P, P]),
+            "moe_dispatch_workspace_bytes": (SZ, [S]),
+            "moe_dispatch": (ctypes.c_int, [S, ctypes.c_int, P, P, P, P, P, P, P, P, P]),
+            "moe_grouped_gemm_workspace_bytes": (SZ, [S, ctypes.c_int]),
+            "moe_grouped_gemm": (ctypes.c_int, [S, ctypes.c_int, P, P, P, P, P, P, P, P]),
+            "moe_combine": (ctypes.c_int, [S, ctypes.c_int, P, P, P, P, P]),
+        }
+        for name, (res, args) in sigs.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def lib():
+    """The loaded ctypes library (raises ImportError when it is not built)."""
+    return _load()
+
+
+def declared_symbols() -> list[str]:
+    """Function names declared in include/moe.h."""
+    with open(header_path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+
+
+def status_string(status: int) -> str:
+    try:
+        return _load().moe_status_string(int(status)).decode()
+    except ImportError:
+        return f"status {status}"
+
+
+def _check(status: int, where: str) -> None:
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+# ----------------------------------------------------------------------------- torch helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("every tensor must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("every tensor must be contiguous (row-major)")
+
+
+def shape(T, d, d_ff, E, k, e_begin, e_end) -> moe_shape:
+    return moe_shape(int(T), int(d), int(d_ff), int(E), int(k), int(e_begin), int(e_end))
+
+
+def expert_range(E: int, ep: int, rank: int) -> tuple[int, int]:
+    lo, hi = ctypes.c_int32(), ctypes.c_int32()
+    _check(_load().moe_expert_range(E, ep, rank, ctypes.byref(lo), ctypes.byref(hi)), "moe_expert_range")
+    return lo.value, hi.value
+
+
+# ----------------------------------------------------------------------------- the four steps
+
+def route_topk(logits, k: int, topk_idx=None, topk_w=None, stream=None):
+    """logits [T, E] fp32 -> (topk_idx [T, k] int32, topk_w [T, k] fp32)."""
+    torch = _torch()
+    _dev(logits)
+    if logits.dtype != torch.float32 or logits.dim() != 2:
+        raise TypeError("logits must be a [T, E] float32 tensor")
+    T, E = logits.shape
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _dev(topk_idx, topk_w)
+    s = shape(T, 8, 8, E, k, 0, E)
+    _check(_load().moe_route_topk(ctypes.byref(s), _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _stream(stream)),
+           "moe_route_topk")
+    return topk_idx, topk_w
+
+
+@dataclass
+class Dispatch:
+    counts: object
+    offsets: object
+    perm: object
+    pair_pos: object
+    x_perm: object
+    workspace: object
+
+
+def dispatch_alloc(x, k: int, E: int, e_begin: int, e_end: int) -> Dispatch:
+    """Allocate every dispatch output (sized on the host, no device read)."""
+    torch = _torch()
+    T, d = x.shape
+    n_max = T * min(k, e_end - e_begin)
+    s = shape(T, d, 8, E, k, e_begin, e_end)
+    ws_bytes = _load().moe_dispatch_workspace_bytes(ctypes.byref(s))
+    dev = x.device
+    return Dispatch(
+        counts=torch.empty(E, dtype=torch.int32, device=dev),
+        offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+        perm=torch.empty(T * k, dtype=torch.int32, device=dev),
+        pair_pos=torch.empty(T * k, dtype=torch.int32, device=dev),
+        x_perm=torch.empty((n_max, d), dtype=x.dtype, device=dev),
+        workspace=torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev),
+    )
+
+
+def dispatch(x, topk_idx, E: int, e_begin: int, e_end: int, out: Dispatch | None = None, stream=None) -> Dispatch:
+    """Histogram, offsets, stable permutation and local-row gather."""
+    _dev(x, topk_idx)
+    T, d = x.shape
+    k = topk_idx.shape[1] if topk_idx.dim() == 2 else 1
+    if out is None:
+        out = dispatch_alloc(x, k, E, e_begin, e_end)
+    s = shape(T, d, 8, E, k, e_begin, e_end)
+    _check(_load().moe_dispatch(ctypes.byref(s), _dtype_code(x), _ptr(x), _ptr(topk_idx), _ptr(out.counts),
+                                _ptr(out.offsets), _ptr(out.perm), _ptr(out.pair_pos), _ptr(out.x_perm),
+                                _ptr(out.workspace), _stream(stream)), "moe_dispatch")
+    return out
+
+
+def grouped_gemm(x_perm, offsets, w_gate_up, w_down, T: int, k: int, E: int, e_begin: int, e_end: int,
+                 h=None, y=None, stream=None):
+    """Local experts' SwiGLU FFN: returns (h [N_max, d_ff], y [N_max, d])."""
+    torch = _torch()
+    _dev(x_perm, offsets, w_gate_up, w_down)
+    n_max, d = x_perm.shape
+    e_loc, d_ff, _ = w_down.shape
+    if w_gate_up.shape != (e_loc, d, 2 * d_ff) or w_down.shape != (e_loc, d_ff, d):
+        raise ValueError("w_gate_up must be [E_loc, d, 2*d_ff] and w_down [E_loc, d_ff, d]")
+    if e_loc != e_end - e_begin:
+        raise ValueError("expert weights must hold exactly the local experts")
+    if h is None:
+        h = torch.empty((n_max, d_ff), dtype=x_perm.dtype, device=x_perm.device)
+    if y is None:
+        y = torch.empty((n_max, d), dtype=x_perm.dtype, device=x_perm.device)
+    _dev(h, y)
+    s = shape(T, d, d_ff, E, k, e_begin, e_end)
+    dt = _dtype_code(x_perm)
+    ws_bytes = _load().moe_grouped_gemm_workspace_bytes(ctypes.byref(s), dt)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=x_perm.device) if ws_bytes else None
+    _check(_load().moe_grouped_gemm(ctypes.byref(s), dt, _ptr(x_perm), _ptr(offsets), _ptr(w_gate_up),
+                                    _ptr(w_down), _ptr(h), _ptr(y), _ptr(ws), _stream(stream)),
+           "moe_grouped_gemm")
+    return h, y
+
+
+def combine(y, pair_pos, topk_w, T: int, k: int, E: int, e_begin: int, e_end: int, out=None, stream=None):
+    """out[t] = sum_j topk_w[t, j] * y[pair_pos[t*k + j]] over local pairs; [T, d]."""
+    torch = _torch()
+    _dev(y, pair_pos, topk_w)
+    d = y.shape[1]
+    if out is None:
+        out = torch.empty((T, d), dtype=y.dtype, device=y.device)
+    _dev(out)
+    s = shape(T, d, 8, E, k, e_begin, e_end)
+    _check(_load().moe_combine(ctypes.byref(s), _dtype_code(y), _ptr(y), _ptr(pair_pos), _ptr(topk_w),
+                               _ptr(out), _stream(stream)), "moe_combine")
+    return out
+
+
+def layer(x, logits, w_gate_up, w_down, k: int, e_begin: int, e_end: int, stream=None) -> dict:
+    """The whole forward of one rank: route -> dispatch -> grouped GEMM -> combine."""
+    T = x.shape[0]
+    E = logits.shape[1]
+    idx, w = route_topk(logits, k, stream=stream)
+    disp = dispatch(x, idx, E, e_begin, e_end, stream=stream)
+    h, y = grouped_gemm(disp.x_perm, disp.offsets, w_gate_up, w_down, T, k, E, e_begin, e_end, stream=stream)
+    out = combine(y, disp.pair_pos, w, T, k, E, e_begin, e_end, stream=stream)
+    return dict(idx=idx, w=w, counts=disp.counts, offsets=disp.offsets, perm=disp.perm,
+                pair_pos=disp.pair_pos, x_perm=disp.x_perm, h=h, y=y, out=out)

@@ -1,0 +1,126 @@
+// Weighted combine of the expert outputs back to token order.
+//
+// What is computed follows "Paralelismo de especialistas" (transformers v5.23.0,
+// pt), sections "Despacho de tokens" (results are combined with the routing
+// weights) and "Adicionando uma implementação" (the weighted expert output of
+// every token the rank holds): out[t] = sum_j w[t,j] * y[pair_pos[t*k+j]] over
+// the token's local pairs, in slot order, in fp32; zero if it has none.
+//
+// Design: one wave per token (grid-stride). The token's k row indices and
+// weights are wave-uniform scalar loads; each lane owns 16-byte column chunks
+// and keeps kChunks of them in flight per slot, so a token issues k * kChunks
+// independent 16-byte loads per lane. HBM-bound: N_loc*d*b read + T*d*b written.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kChunks = 4;  // 16-byte chunks per lane per pass
+
+template <bool BF16>
+struct Vec;
+
+template <>
+struct Vec<true> {  // 8 bf16 per 16 bytes
+  static constexpr int kN = 8;
+  __device__ static void load(const uint4& v, float* f) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+  __device__ static uint4 store(const float* f) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(f32_to_bf16_rne(f[2 * i])) |
+             (static_cast<uint32_t>(f32_to_bf16_rne(f[2 * i + 1])) << 16);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+
+template <>
+struct Vec<false> {  // 4 fp32 per 16 bytes
+  static constexpr int kN = 4;
+  __device__ static void load(const uint4& v, float* f) {
+    f[0] = __uint_as_float(v.x);
+    f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z);
+    f[3] = __uint_as_float(v.w);
+  }
+  __device__ static uint4 store(const float* f) {
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                      __float_as_uint(f[3]));
+  }
+};
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void combine_kernel(const uint4* __restrict__ y,
+                                                           const int32_t* __restrict__ pair_pos,
+                                                           const float* __restrict__ w,
+                                                           uint4* __restrict__ out, int64_t T, int k,
+                                                           int row_vec, int64_t n_max) {
+  using V = Vec<BF16>;
+  const int lane = lane_id();
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kThreads / kWave);
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave; t < T;
+       t += nwaves) {
+    for (int c0 = 0; c0 < row_vec; c0 += kChunks * kWave) {
+      float acc[kChunks][V::kN];
+#pragma unroll
+      for (int q = 0; q < kChunks; ++q)
+#pragma unroll
+        for (int i = 0; i < V::kN; ++i) acc[q][i] = 0.f;
+      for (int j = 0; j < k; ++j) {
+        const int r = pair_pos[t * k + j];
+        if (r < 0 || r >= n_max) continue;
+        const float wj = w[t * k + j];
+        const uint4* src = y + static_cast<int64_t>(r) * row_vec;
+        uint4 v[kChunks];
+#pragma unroll
+        for (int q = 0; q < kChunks; ++q) {
+          const int c = c0 + q * kWave + lane;
+          v[q] = c < row_vec ? src[c] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < kChunks; ++q) {
+          float f[V::kN];
+          V::load(v[q], f);
+#pragma unroll
+          for (int i = 0; i < V::kN; ++i) acc[q][i] = fmaf(wj, f[i], acc[q][i]);
+        }
+      }
+      uint4* dst = out + t * row_vec;
+#pragma unroll
+      for (int q = 0; q < kChunks; ++q) {
+        const int c = c0 + q * kWave + lane;
+        if (c < row_vec) dst[c] = V::store(acc[q]);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const void* y, const int32_t* pair_pos, const float* w, void* out,
+                          int64_t T, int k, int d, int64_t n_max, bool bf16, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const int row_vec = bf16 ? d / 8 : d / 4;
+  int64_t blocks = (T + (kThreads / kWave) - 1) / (kThreads / kWave);
+  if (blocks > 4096) blocks = 4096;
+  if (bf16) {
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                       stream, static_cast<const uint4*>(y), pair_pos, w, static_cast<uint4*>(out), T,
+                       k, row_vec, n_max);
+  } else {
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                       stream, static_cast<const uint4*>(y), pair_pos, w, static_cast<uint4*>(out), T,
+                       k, row_vec, n_max);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

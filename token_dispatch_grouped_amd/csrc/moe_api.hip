@@ -1,0 +1,140 @@
+// C ABI of the MoE expert-layer forward: host-side validation, then launches.
+// Every check runs before anything is enqueued, so an invalid call touches no
+// output ("Paralelismo de especialistas", section "Sobrescrevendo os planos":
+// errors are raised before anything is sharded).
+#include <limits.h>
+
+#include "moe_internal.h"
+
+namespace {
+
+using moe::kMaxExperts;
+
+moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+// Shape checks shared by the layer steps. `need_dims` adds d/d_ff/local-range checks.
+moe_status check_shape(const moe_shape* s, bool need_dims) {
+  if (s == nullptr) return MOE_EINVAL;
+  if (s->T < 0 || s->E < 1 || s->k < 1 || s->k > s->E) return MOE_EINVAL;
+  if (s->T * static_cast<int64_t>(s->k) > INT32_MAX) return MOE_EINVAL;
+  if (s->E > kMaxExperts) return MOE_EUNSUPPORTED;
+  if (need_dims) {
+    if (s->d <= 0 || s->d_ff <= 0 || s->d % 8 != 0 || s->d_ff % 8 != 0) return MOE_EINVAL;
+    if (s->e_begin < 0 || s->e_end > s->E || s->e_begin >= s->e_end) return MOE_EINVAL;
+  }
+  return MOE_OK;
+}
+
+bool valid_dtype(moe_dtype dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+
+size_t elem_bytes(moe_dtype dt) { return dt == MOE_BF16 ? 2 : 4; }
+
+int64_t n_max_of(const moe_shape* s) {
+  const int64_t e_loc = s->e_end - s->e_begin;
+  return s->T * (s->k < e_loc ? s->k : e_loc);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: unsupported shape";
+    case MOE_EHIP: return "MOE_EHIP: HIP launch failed";
+  }
+  return "unknown moe_status";
+}
+
+moe_status moe_expert_range(int32_t E, int32_t ep, int32_t rank, int32_t* e_begin, int32_t* e_end) {
+  if (e_begin == nullptr || e_end == nullptr) return MOE_EINVAL;
+  if (E < 1 || ep < 1 || E % ep != 0 || rank < 0) return MOE_EINVAL;
+  const int32_t per = E / ep;
+  const int32_t r = rank % ep;
+  *e_begin = r * per;
+  *e_end = (r + 1) * per;
+  return MOE_OK;
+}
+
+moe_status moe_route_topk(const moe_shape* s, const float* logits, int32_t* topk_idx, float* topk_w,
+                          hipStream_t stream) {
+  const moe_status st = check_shape(s, false);
+  if (st != MOE_OK) return st;
+  if (s->T == 0) return MOE_OK;
+  if (logits == nullptr || topk_idx == nullptr || topk_w == nullptr) return MOE_EINVAL;
+  if (s->T * static_cast<int64_t>(s->E) > (int64_t{1} << 40)) return MOE_EUNSUPPORTED;
+  return from_hip(moe::launch_route_topk(logits, topk_idx, topk_w, s->T, s->E, s->k, stream));
+}
+
+size_t moe_dispatch_workspace_bytes(const moe_shape* s) {
+  if (check_shape(s, false) != MOE_OK) return 0;
+  return moe::dispatch_workspace_bytes(s->T, s->k, s->E);
+}
+
+moe_status moe_dispatch(const moe_shape* s, moe_dtype dt, const void* x, const int32_t* topk_idx,
+                        int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pair_pos,
+                        void* x_perm, void* workspace, hipStream_t stream) {
+  const moe_status st = check_shape(s, true);
+  if (st != MOE_OK) return st;
+  if (!valid_dtype(dt)) return MOE_EINVAL;
+  if (counts == nullptr || offsets == nullptr) return MOE_EINVAL;
+  if (s->T > 0) {
+    if (x == nullptr || topk_idx == nullptr || perm == nullptr || pair_pos == nullptr ||
+        x_perm == nullptr)
+      return MOE_EINVAL;
+    if (moe::dispatch_workspace_bytes(s->T, s->k, s->E) > 0 && workspace == nullptr) return MOE_EINVAL;
+  }
+  return from_hip(moe::launch_dispatch(x, static_cast<size_t>(s->d) * elem_bytes(dt), topk_idx, counts,
+                                       offsets, perm, pair_pos, x_perm, workspace, s->T, s->k, s->E,
+                                       s->e_begin, s->e_end, n_max_of(s), stream));
+}
+
+size_t moe_grouped_gemm_workspace_bytes(const moe_shape* s, moe_dtype dt) {
+  (void)s;
+  (void)dt;
+  return 0;
+}
+
+moe_status moe_grouped_gemm(const moe_shape* s, moe_dtype dt, const void* x_perm,
+                            const int32_t* offsets, const void* w_gate_up, const void* w_down, void* h,
+                            void* y, void* workspace, hipStream_t stream) {
+  (void)workspace;
+  const moe_status st = check_shape(s, true);
+  if (st != MOE_OK) return st;
+  if (!valid_dtype(dt)) return MOE_EINVAL;
+  if (s->T == 0) return MOE_OK;
+  if (x_perm == nullptr || offsets == nullptr || w_gate_up == nullptr || w_down == nullptr ||
+      h == nullptr || y == nullptr)
+    return MOE_EINVAL;
+  const int e_loc = s->e_end - s->e_begin;
+  const int64_t n_max = n_max_of(s);
+  // Per-expert weights are addressed through 32-bit buffer offsets (with one
+  // K step of slack for the tail); larger experts are not supported.
+  const int64_t eb = static_cast<int64_t>(elem_bytes(dt));
+  if ((static_cast<int64_t>(s->d) + 64) * 2 * s->d_ff * eb > INT32_MAX ||
+      (static_cast<int64_t>(s->d_ff) + 64) * s->d * eb > INT32_MAX)
+    return MOE_EUNSUPPORTED;
+  if (dt == MOE_BF16)
+    return from_hip(moe::launch_grouped_gemm_bf16(x_perm, offsets, w_gate_up, w_down, h, y, s->d,
+                                                  s->d_ff, s->e_begin, e_loc, n_max, s->T, s->k,
+                                                  s->E, stream));
+  return from_hip(moe::launch_grouped_gemm_f32(
+      static_cast<const float*>(x_perm), offsets, static_cast<const float*>(w_gate_up),
+      static_cast<const float*>(w_down), static_cast<float*>(h), static_cast<float*>(y), s->d, s->d_ff,
+      s->e_begin, e_loc, n_max, stream));
+}
+
+moe_status moe_combine(const moe_shape* s, moe_dtype dt, const void* y, const int32_t* pair_pos,
+                       const float* topk_w, void* out, hipStream_t stream) {
+  const moe_status st = check_shape(s, true);
+  if (st != MOE_OK) return st;
+  if (!valid_dtype(dt)) return MOE_EINVAL;
+  if (s->T == 0) return MOE_OK;
+  if (y == nullptr || pair_pos == nullptr || topk_w == nullptr || out == nullptr) return MOE_EINVAL;
+  return from_hip(moe::launch_combine(y, pair_pos, topk_w, out, s->T, s->k, s->d, n_max_of(s),
+                                      dt == MOE_BF16, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// Internal helpers and launcher declarations shared by the HIP sources.
+// Target: gfx950 (CDNA4), wave64.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kMaxExperts = 1024;
+
+// Pairs handled by one dispatch workgroup (256 threads x 4 passes).
+constexpr int kDispatchChunk = 1024;
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Wave-uniform value as an SGPR (the caller guarantees uniformity).
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) & (kWave - 1); }
+
+// Launchers (host side). Each returns hipSuccess or the launch error.
+hipError_t launch_route_topk(const float* logits, int32_t* idx, float* w, int64_t T, int E, int k,
+                             hipStream_t stream);
+
+size_t dispatch_workspace_bytes(int64_t T, int k, int E);
+hipError_t launch_dispatch(const void* x, size_t row_bytes, const int32_t* idx, int32_t* counts,
+                           int32_t* offsets, int32_t* perm, int32_t* pair_pos, void* x_perm,
+                           void* workspace, int64_t T, int k, int E, int e_begin, int e_end,
+                           int64_t n_max, hipStream_t stream);
+
+hipError_t launch_grouped_gemm_bf16(const void* x_perm, const int32_t* offsets, const void* w_gu,
+                                    const void* w_dn, void* h, void* y, int d, int d_ff, int e_begin,
+                                    int e_loc, int64_t n_max, int64_t T, int k, int E,
+                                    hipStream_t stream);
+hipError_t launch_grouped_gemm_f32(const float* x_perm, const int32_t* offsets, const float* w_gu,
+                                   const float* w_dn, float* h, float* y, int d, int d_ff,
+                                   int e_begin, int e_loc, int64_t n_max, hipStream_t stream);
+
+hipError_t launch_combine(const void* y, const int32_t* pair_pos, const float* w, void* out,
+                          int64_t T, int k, int d, int64_t n_max, bool bf16, hipStream_t stream);
+
+}  // namespace moe

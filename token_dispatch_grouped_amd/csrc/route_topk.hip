@@ -1,0 +1,135 @@
+// Router top-k with softmax over the selected logits, one token per lane group.
+//
+// What is computed follows "Paralelismo de especialistas" (transformers v5.23.0,
+// pt), section "Adicionando uma implementação" (top_k_index / top_k_weights):
+// the k largest logits of each token in descending order, equal logits to the
+// lower expert id (signed zeros equal), and weights = softmax of those k logits.
+//
+// Design: G lanes (a power of two, G <= 64) share one token and each lane keeps
+// VPL logits in registers, expert e = g + v*G, so a group's loads are contiguous.
+// A logit and its id form one 64-bit key (order-preserving float bits << 32 |
+// ~id), so "larger value, then lower id" is a plain unsigned max and every key
+// is unique. Each of the k rounds is a register max plus a log2(G)-step
+// butterfly; the owning lane then retires its key. HBM-bound: T*E*4 bytes read.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+__device__ __forceinline__ uint32_t orderable(float v) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;  // -0.0 ranks as +0.0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float from_orderable(uint32_t o) {
+  const uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
+  const int lo = __shfl_xor(static_cast<int>(static_cast<uint32_t>(v)), mask);
+  const int hi = __shfl_xor(static_cast<int>(static_cast<uint32_t>(v >> 32)), mask);
+  return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+}
+
+template <int G, int VPL>
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits,
+                                                         int32_t* __restrict__ idx,
+                                                         float* __restrict__ w, int64_t T, int E,
+                                                         int k) {
+  constexpr int kTokensPerWave = kWave / G;
+  const int lane = lane_id();
+  const int g = lane % G;
+  const int64_t wave = static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int64_t t = wave * kTokensPerWave + lane / G;
+  const bool active = t < T;
+
+  uint64_t key[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    const int e = g + v * G;
+    key[v] = 0;
+    if (active && e < E) {
+      const float x = logits[t * E + e];
+      key[v] = (static_cast<uint64_t>(orderable(x)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(e));
+    }
+  }
+
+  // Round r's result is kept by lane r % G in slot r / G (r < k <= E <= G*VPL).
+  float sel_val[VPL];
+  int sel_id[VPL];
+#pragma unroll
+  for (int s = 0; s < VPL; ++s) {
+    sel_val[s] = 0.f;
+    sel_id[s] = 0;
+  }
+  float top = 0.f, sum = 0.f;
+  for (int r = 0; r < k; ++r) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int v = 1; v < VPL; ++v) best = key[v] > best ? key[v] : best;
+#pragma unroll
+    for (int off = G / 2; off > 0; off >>= 1) {
+      const uint64_t o = shfl_xor_u64(best, off);
+      best = o > best ? o : best;
+    }
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+      if (key[v] == best) key[v] = 0;  // keys are unique: only the owner matches
+    const float val = from_orderable(static_cast<uint32_t>(best >> 32));
+    const int id = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(best));
+    if (r == 0) top = val;
+    sum += expf(val - top);
+    if (r % G == g) {
+#pragma unroll
+      for (int s = 0; s < VPL; ++s)
+        if (s == r / G) {
+          sel_val[s] = val;
+          sel_id[s] = id;
+        }
+    }
+  }
+  if (!active) return;
+  const float inv = 1.0f / sum;
+#pragma unroll
+  for (int s = 0; s < VPL; ++s) {
+    const int r = s * G + g;
+    if (r < k) {
+      idx[t * k + r] = sel_id[s];
+      w[t * k + r] = expf(sel_val[s] - top) * inv;
+    }
+  }
+}
+
+template <int G, int VPL>
+hipError_t launch_g(const float* logits, int32_t* idx, float* w, int64_t T, int E, int k,
+                    hipStream_t stream) {
+  constexpr int kThreads = 256;
+  constexpr int64_t kTokensPerBlock = (kThreads / kWave) * (kWave / G);
+  const int64_t blocks = (T + kTokensPerBlock - 1) / kTokensPerBlock;
+  hipLaunchKernelGGL((route_topk_kernel<G, VPL>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
+                     0, stream, logits, idx, w, T, E, k);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_route_topk(const float* logits, int32_t* idx, float* w, int64_t T, int E, int k,
+                             hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  // group size G = next power of two >= E, capped at a wave; VPL = values per lane
+  if (E <= 1) return launch_g<1, 1>(logits, idx, w, T, E, k, stream);
+  if (E <= 2) return launch_g<2, 1>(logits, idx, w, T, E, k, stream);
+  if (E <= 4) return launch_g<4, 1>(logits, idx, w, T, E, k, stream);
+  if (E <= 8) return launch_g<8, 1>(logits, idx, w, T, E, k, stream);
+  if (E <= 16) return launch_g<16, 1>(logits, idx, w, T, E, k, stream);
+  if (E <= 32) return launch_g<32, 1>(logits, idx, w, T, E, k, stream);
+  if (E <= 64) return launch_g<64, 1>(logits, idx, w, T, E, k, stream);
+  if (E <= 128) return launch_g<64, 2>(logits, idx, w, T, E, k, stream);
+  if (E <= 256) return launch_g<64, 4>(logits, idx, w, T, E, k, stream);
+  if (E <= 512) return launch_g<64, 8>(logits, idx, w, T, E, k, stream);
+  return launch_g<64, 16>(logits, idx, w, T, E, k, stream);
+}
+
+}  // namespace moe
