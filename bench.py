@@ -1,0 +1,178 @@
+"""Benchmark: routed tokens/s of one rank's MoE expert-layer forward on one MI355X.
+
+A step is the whole path on one batch already resident in HBM: route top-k ->
+dispatch -> grouped GEMM (gate/up + SwiGLU, then down) -> combine, through the
+C ABI, with every buffer allocated before timing. Prints ONE JSON line.
+
+The roofline object covers the grouped GEMM (both of its MFMA launches), timed
+with events recorded on the stream the kernels run on. The CPU baseline is the
+fp64 oracle on a bounded sample of the same workload, timed on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import moe_inputs as mi  # noqa: E402
+
+METRIC = "routed tokens/sec per MoE layer fwd on 1 MI355X; grouped-GEMM % MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0
+
+
+def host_cores() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit():
+        n = min(n, int(omp))
+    return n
+
+
+def cpu_baseline(w: mi.Workload, logits, x, wgu, wdn, budget_s: float = 12.0) -> dict:
+    """The oracle, as it stands, on the first T_s tokens of the same workload."""
+    import oracle
+
+    x64 = mi.to_f64(x, w.dtype)
+    gu64 = [mi.to_f64(wgu[e], w.dtype) for e in range(w.E_loc)]
+    dn64 = [mi.to_f64(wdn[e], w.dtype) for e in range(w.E_loc)]
+    ts = min(w.T, 64)
+    while True:
+        t0 = time.perf_counter()
+        oracle.moe_layer(x64[:ts], logits[:ts], w.k, w.e_begin, w.e_end, gu64, dn64)
+        dt = time.perf_counter() - t0
+        if dt * 2 > budget_s or ts >= w.T:
+            break
+        ts = min(w.T, ts * 2)
+    return {"value": ts / dt, "unit": "tokens/s", "cores": host_cores(), "kind": "oracle",
+            "sample": f"oracle.moe_layer (fp64, numpy BLAS) on the first {ts} of {w.T} tokens of "
+                      f"workload {w.name}, {dt:.2f} s; fp64 weight conversion untimed"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dense8", choices=sorted(mi.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the layer; --gpus {args.gpus} is not supported "
+              "(the multi-GPU exchange is not part of this library)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import token_dispatch_grouped_amd as moe
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    w = mi.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    logits = mi.router_logits(w)
+    x = mi.hidden_states(w)
+    wgu, wdn = mi.expert_weights(w)
+    print(f"[bench] inputs for {w.name} drawn in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    def to_dev(a, dtype):
+        if dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    dx, dl = to_dev(x, w.dtype), to_dev(logits, "f32")
+    dgu, ddn = to_dev(wgu, w.dtype), to_dev(wdn, w.dtype)
+    # every buffer the step writes, allocated once
+    idx = torch.empty((w.T, w.k), dtype=torch.int32, device=dev)
+    wts = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
+    disp = moe.dispatch_alloc(dx, w.k, w.E, w.e_begin, w.e_end)
+    h = torch.empty((w.n_max, w.d_ff), dtype=dx.dtype, device=dev)
+    y = torch.empty((w.n_max, w.d), dtype=dx.dtype, device=dev)
+    out = torch.empty((w.T, w.d), dtype=dx.dtype, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+
+    def step(i=None):
+        moe.route_topk(dl, w.k, idx, wts, stream=stream)
+        moe.dispatch(dx, idx, w.E, w.e_begin, w.e_end, out=disp, stream=stream)
+        if i is not None:
+            ev[i][0].record(stream)
+        moe.grouped_gemm(disp.x_perm, disp.offsets, dgu, ddn, w.T, w.k, w.E, w.e_begin, w.e_end,
+                         h=h, y=y, stream=stream)
+        if i is not None:
+            ev[i][1].record(stream)
+        moe.combine(y, disp.pair_pos, wts, w.T, w.k, w.E, w.e_begin, w.e_end, out=out, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    offs = disp.offsets.cpu().numpy()
+    n_loc = int(offs[w.e_end] - offs[w.e_begin])
+    active = int(np.count_nonzero(disp.counts.cpu().numpy()[w.e_begin:w.e_end]))
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+    gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    flops = 6.0 * n_loc * w.d * w.d_ff  # gate/up (4 N d d_ff) + down (2 N d d_ff)
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    achieved = flops / (gemm_ms * 1e-3) / 1e12
+    roofline = {
+        "kernel": "moe_grouped_gemm (gate/up+SwiGLU launch, then down launch)",
+        "bound": "mfma" if w.dtype == "bf16" else "alu",
+        "achieved": round(achieved, 2),
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / peak, 4),
+        "traffic": None,
+        "flops_per_launch": flops,
+        "avg_ms": round(gemm_ms, 4),
+    }
+    result = {
+        "metric": METRIC,
+        "value": round(w.T / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded normal draws; see moe_inputs)",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "d_ff": w.d_ff, "E": w.E, "k": w.k,
+                   "local_experts": [w.e_begin, w.e_end], "N_loc": n_loc, "active_local_experts": active,
+                   "parallelism": "one rank's share on 1 GPU"},
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    del dgu, ddn
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, logits, x, wgu, wdn)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
