@@ -224,3 +224,33 @@ def test_layer_is_deterministic():
         if ta.dtype == torch.bfloat16:
             ta, tb = ta.view(torch.int16), tb.view(torch.int16)
         assert torch.equal(ta, tb), key
+
+
+def _one_hot_logits(counts, E, seed):
+    """Router logits that send exactly counts[e] tokens to expert e as their top-1."""
+    rng = np.random.default_rng(seed)
+    T = int(sum(counts))
+    owner = np.repeat(np.arange(len(counts)), counts)
+    rng.shuffle(owner)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[np.arange(T), owner] += 50.0
+    return logits
+
+
+def test_layer_every_tile_height():
+    """Experts whose row counts hit every tail-tile height (32/64/128/256) and the edges."""
+    counts = [0, 1, 31, 32, 33, 64, 65, 128, 129, 255, 256, 257, 300, 513]
+    E = len(counts)
+    w = mi.Workload("tile_heights", int(sum(counts)), 256, 160, E, 1, 0, E, "bf16", 23)
+    res, ref = _layer_case(w, _one_hot_logits(counts, E, 23))
+    top1 = ref["idx"][:, 0]
+    assert [int((top1 == e).sum()) for e in range(E)] == counts
+
+
+@pytest.mark.parametrize("w", [SMALL[3], SMALL[4], mi.Workload("regs_heights", 600, 256, 192, 8, 2, 0, 8, "bf16", 24)],
+                         ids=["skew_small", "decode_small", "heights"])
+def test_layer_register_staged_kernel(w, monkeypatch):
+    """The register-staged GEMM (used when d or d_ff is not a multiple of 32) on
+    shapes the pipelined kernel would otherwise take."""
+    monkeypatch.setenv("MOE_GEMM_KERNEL", "regs")
+    _layer_case(w)

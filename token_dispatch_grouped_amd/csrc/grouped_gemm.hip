@@ -40,123 +40,25 @@
 //     resource ends at the tile's last valid row.
 //
 // fp32 (small parity workload): a plain VALU tiled kernel with the same tile walk.
-#include "moe_internal.h"
+#include <stdlib.h>
+#include <string.h>
+
+#include "gemm_common.h"
 
 namespace moe {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
+using namespace gemm;
 
 constexpr int kBM = 256;       // rows per tile
 constexpr int kBN = 256;       // weight columns per tile (128 gate + 128 up for SwiGLU)
 constexpr int kBK = 64;        // K per pipeline step
-constexpr int kThreads = 256;  // 4 waves
 constexpr int kTileElems = 256 * kBK;
-
-// Per-workgroup tile prefix over the local experts, derived from the device offsets.
-struct TileMap {
-  int mstart[kMaxExperts + 1];  // row-tile prefix per expert
-  int rstart[kMaxExperts + 1];  // first row of each expert, relative to the local segment
-};
-
-// Rows are clamped to [0, n_max): with a caller-supplied topk_idx that repeats an
-// id inside a token, local pairs could exceed n_max; those rows are dropped
-// rather than written past the end of H and Y.
-template <int BM>
-__device__ void build_tile_map(TileMap& tm, const int32_t* __restrict__ offsets, int e_begin,
-                               int e_loc, int n_max) {
-  if (threadIdx.x < kWave) {
-    const int lane = threadIdx.x;
-    const int base = offsets[e_begin];
-    int carry = 0;
-    for (int e0 = 0; e0 < e_loc; e0 += kWave) {
-      const int e = e0 + lane;
-      int rows = 0, start = 0;
-      if (e < e_loc) {
-        start = min(offsets[e_begin + e] - base, n_max);
-        rows = min(offsets[e_begin + e + 1] - base, n_max) - start;
-      }
-      const int mt = (rows + BM - 1) / BM;
-      int incl = mt;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const int o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-      }
-      if (e < e_loc) {
-        tm.mstart[e] = carry + incl - mt;
-        tm.rstart[e] = start;
-      }
-      carry += __shfl(incl, kWave - 1);
-    }
-    if (lane == 0) {
-      tm.mstart[e_loc] = carry;
-      tm.rstart[e_loc] = min(offsets[e_begin + e_loc] - base, n_max);
-    }
-  }
-  __syncthreads();
-}
-
-struct TileCoord {
-  int e, mt, nt;
-};
-
-// Expert e with mstart[e]*n_tiles <= tile < mstart[e+1]*n_tiles (empty experts own no ids).
-__device__ __forceinline__ TileCoord find_tile(const TileMap& tm, int tile, int n_tiles, int e_loc) {
-  int lo = 0, hi = e_loc;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (tm.mstart[mid] * n_tiles <= tile) lo = mid;
-    else hi = mid;
-  }
-  // values read from LDS are not known to be wave-uniform: pin them to SGPRs
-  lo = uniform(lo);
-  const int ms = uniform(tm.mstart[lo]);
-  const int mt_e = uniform(tm.mstart[lo + 1]) - ms;
-  const int local = tile - ms * n_tiles;
-  return {lo, local % mt_e, local / mt_e};
-}
-
-// Workgroup -> first tile id: each XCD (workgroups are dealt to the 8 XCDs
-// round-robin) gets a contiguous range of ids.
-__device__ __forceinline__ int xcd_remap(int b, int G) {
-  return (G & 7) == 0 ? (b & 7) * (G >> 3) + (b >> 3) : b;
-}
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
 // LDS element offset of the 16-byte chunk c (0..7) of row r of a [256][64] tile.
 __device__ __forceinline__ int lds_off(int r, int c) { return r * kBK + ((c ^ swz(r)) << 3); }
-
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
-
-// SiLU for results that are rounded to bf16 next: hardware exp2 and reciprocal,
-// a few ulp of fp32, far below bf16's half-ulp of 2^-9.
-__device__ __forceinline__ float silu_fast(float g) {
-  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-}
-
-// Hides a value from loop-invariant code motion, so offsets derived from it are
-// recomputed (one add each) instead of being hoisted into many live registers.
-template <typename T>
-__device__ __forceinline__ T opaque(T v) {
-  asm volatile("" : "+v"(v));
-  return v;
-}
-
-// Raw buffer resource over [base, base + bytes): loads past the end return 0.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
-                                           0x00020000);
-}
-
-__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset) {
-  typedef int i32x4_t __attribute__((ext_vector_type(4)));
-  const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, static_cast<int>(voffset), 0, 0);
-  return make_uint4(static_cast<uint32_t>(v.x), static_cast<uint32_t>(v.y), static_cast<uint32_t>(v.z),
-                    static_cast<uint32_t>(v.w));
-}
 
 template <bool SWIGLU>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
@@ -411,11 +313,18 @@ hipError_t launch_grouped_gemm_bf16(const void* x_perm, const int32_t* offsets, 
   (void)E;
   if (n_max == 0) return hipSuccess;
   const int g1 = grid_for(n_max, e_loc, kBM, (d_ff + 127) / 128, 1);
+  const int g2 = grid_for(n_max, e_loc, kBM, (d + 255) / 256, 1);
+  // The LDS-pipelined kernel needs K (d for gate/up, d_ff for down) in whole
+  // 32-wide stages; MOE_GEMM_KERNEL=regs forces the register-staged kernel.
+  const char* force = getenv("MOE_GEMM_KERNEL");
+  const bool regs = force != nullptr && strcmp(force, "regs") == 0;
+  if (!regs && d % 32 == 0 && d_ff % 32 == 0)
+    return launch_grouped_gemm_lds(x_perm, offsets, w_gu, w_dn, h, y, d, d_ff, e_begin, e_loc, n_max, g1, g2,
+                                   stream);
   hipLaunchKernelGGL(grouped_gemm_bf16_kernel<true>, dim3(g1), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(x_perm), static_cast<const uint16_t*>(w_gu),
                      static_cast<uint16_t*>(h), offsets, e_begin, e_loc, d, d_ff, 2 * d_ff,
                      static_cast<int>(n_max));
-  const int g2 = grid_for(n_max, e_loc, kBM, (d + 255) / 256, 1);
   hipLaunchKernelGGL(grouped_gemm_bf16_kernel<false>, dim3(g2), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_dn),
                      static_cast<uint16_t*>(y), offsets, e_begin, e_loc, d_ff, d, d,

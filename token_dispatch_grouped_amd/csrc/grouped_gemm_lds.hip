@@ -1,0 +1,361 @@
+// Grouped expert GEMM, pipelined variant for K a multiple of 32 (every
+// workload's d and d_ff): operands go from HBM straight into LDS and the
+// N-contiguous weights are read back transposed by the LDS unit.
+//
+// What is computed is the same as the register-staged kernel in
+// grouped_gemm.hip: experts_forward of "Paralelismo de especialistas"
+// (transformers v5.23.0, pt), section "Adicionando uma implementação", on the
+// packed gate_up_proj of "Paralelismo de tensor para inferência", section
+// "Estratégias empacotadas", with SwiGLU = silu(gate) * up, then the down
+// projection.
+//
+// Design (gfx950):
+//   * Four LDS stages of K = 32 (16 KB of activations + 16 KB of weights each,
+//     128 KB in all). Each stage is filled by buffer_load ... lds (16 bytes per
+//     lane, written to LDS without passing through registers), issued three
+//     stages ahead of its use, so about 3 x 1000 MFMA cycles of HBM/L2 latency
+//     are covered without staging registers.
+//   * Activations sit in LDS as [row][32] (64-byte rows) with the 16-byte chunk
+//     index XOR-ed by (row >> 2) & 3; 16 consecutive fragment rows then hit 16
+//     distinct bank groups. Weights sit as [k][256] in the pages' N-contiguous
+//     order with the chunk index XOR-ed by 4 * (k & 3); ds_read_b64_tr_b16 turns
+//     each 4 (k) x 16 (n) block into per-lane 4-k columns, two of which form a
+//     v_mfma_f32_32x32x16_bf16 B operand. No weight repacking, no VALU transpose.
+//   * LDS reads are issued by inline asm with explicit lgkmcnt waits, so the
+//     compiler does not serialise them behind the outstanding LDS-DMA loads;
+//     fragments for the next 16-wide K slice are read while the current slice's
+//     16 MFMAs run, and sched_barriers keep that interleave in place.
+//   * Row tiles are 256 rows, except an expert's last tile, which takes the
+//     smallest of 32/64/128/256 rows that covers it, so a ragged tail costs a
+//     fraction of a full tile. Wave layouts: 2 x 2 waves of (H/2) x 128 for
+//     H >= 64, 1 x 4 waves of 32 x 64 for H = 32.
+//   * Tile walk, XCD mapping and the buffer-store epilogue follow the
+//     register-staged kernel.
+#include "gemm_common.h"
+
+namespace moe {
+namespace {
+
+using namespace gemm;
+
+#define LDS3 __attribute__((address_space(3)))
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kBK = 32;                      // K per stage
+constexpr int kStages = 4;
+constexpr int kStageElems = 256 * kBK;       // bf16 per operand per stage (16 KB)
+constexpr uint32_t kStageBytes = kStageElems * 2;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const LDS3 char*)p));
+}
+
+// Wait until at most n vector-memory operations of this wave are outstanding
+// (n is wave-uniform; rounded down to a count this kernel uses, which only waits longer).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  if (n >= 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if (n >= 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  else if (n >= 10) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+  else if (n >= 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if (n >= 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  else if (n >= 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+  else if (n >= 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_lgkmcnt() {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+  if constexpr (N == 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  else if constexpr (N == 5) asm volatile("s_waitcnt lgkmcnt(5)" ::: "memory");
+  else if constexpr (N == 9) asm volatile("s_waitcnt lgkmcnt(9)" ::: "memory");
+  else if constexpr (N == 10) asm volatile("s_waitcnt lgkmcnt(10)" ::: "memory");
+  else if constexpr (N == 12) asm volatile("s_waitcnt lgkmcnt(12)" ::: "memory");
+  else static_assert(N == 0, "add the count");
+}
+
+template <typename T>
+__device__ __forceinline__ void tie(T& v) {
+  asm volatile("" : "+v"(v));
+}
+
+template <int IMM>
+__device__ __forceinline__ bf16x8_t ds_read16(uint32_t addr) {
+  bf16x8_t v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(IMM));
+  return v;
+}
+
+template <int IMM>
+__device__ __forceinline__ i16x4_t ds_read_tr(uint32_t addr) {
+  i16x4_t v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(IMM));
+  return v;
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS3 void*)lds, 16, voff, 0, 0, 0);
+}
+
+struct Frags {
+  // up to 4 A blocks and 4 B blocks (each B block = two 4-k halves)
+  bf16x8_t a[4];
+  i16x4_t b[4][2];
+};
+
+template <int H>
+struct Layout {
+  static constexpr int WM = H >= 64 ? 2 : 1;       // waves along M
+  static constexpr int WN = 4 / WM;                // waves along N
+  static constexpr int MI = H / WM / 32;           // 32-row MFMA blocks per wave
+  static constexpr int NI = 256 / WN / 32;         // 32-column MFMA blocks per wave
+  static constexpr int A_INSTR = H / 16;           // 1 KB DMA instructions per A stage
+  static constexpr int A_PER_WAVE = A_INSTR >= 4 ? A_INSTR / 4 : 1;
+  static constexpr int LDS_READS = MI + 2 * NI;    // LDS instructions per 16-wide K slice
+};
+
+template <bool SWIGLU, int H>
+__device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __restrict__ A,
+                                          const uint16_t* __restrict__ Bexp, uint16_t* __restrict__ C,
+                                          int row0, int rows_valid, int n0, int K, int N, int ldb) {
+  using L = Layout<H>;
+  constexpr int MI = L::MI, NI = L::NI, WN = L::WN;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = uniform(tid / kWave);
+  const int wm = wave / WN, wn = wave % WN;
+  const int ksteps = K / kBK;
+
+  uint16_t* sA = smem;
+  uint16_t* sB = smem + kStages * kStageElems;
+
+  // ---- DMA issue: per-lane byte offsets (constant over the tile) ----------------
+  const uint16_t* a_tile = A + static_cast<int64_t>(row0) * K;
+  const uint32_t a_bytes = static_cast<uint32_t>(rows_valid) * static_cast<uint32_t>(K) * 2u;
+  const uint32_t b_bytes = static_cast<uint32_t>(K) * static_cast<uint32_t>(ldb) * 2u;
+  uint32_t a_voff[L::A_PER_WAVE];
+  bool a_on[L::A_PER_WAVE];
+#pragma unroll
+  for (int jj = 0; jj < L::A_PER_WAVE; ++jj) {
+    const int j = wave * L::A_PER_WAVE + jj;
+    a_on[jj] = j < L::A_INSTR;
+    const int r = 16 * j + (lane >> 2);
+    const int c = (lane & 3) ^ ((lane >> 4) & 3);
+    a_voff[jj] = static_cast<uint32_t>(r) * static_cast<uint32_t>(K) * 2u + static_cast<uint32_t>(c) * 16u;
+  }
+  uint32_t b_voff[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int j = wave * 4 + jj;
+    const int kl = 2 * j + (lane >> 5);
+    const int c = (lane & 31) ^ (4 * (kl & 3));
+    int col;
+    if (SWIGLU) col = c < 16 ? n0 + 8 * c : N + n0 + 8 * (c - 16);
+    else col = n0 + 8 * c;
+    b_voff[jj] = (static_cast<uint32_t>(kl) * static_cast<uint32_t>(ldb) + static_cast<uint32_t>(col)) * 2u;
+  }
+  const int per_stage = 4 + (a_on[0] ? L::A_PER_WAVE : 0);
+
+  auto issue = [&](int s) {
+    const int buf = s % kStages;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_tile + s * kBK, a_bytes - static_cast<uint32_t>(s) * kBK * 2u);
+    const __amdgpu_buffer_rsrc_t rb =
+        make_rsrc(Bexp + static_cast<int64_t>(s) * kBK * ldb, b_bytes - static_cast<uint32_t>(s) * kBK * ldb * 2u);
+#pragma unroll
+    for (int jj = 0; jj < L::A_PER_WAVE; ++jj)
+      if (a_on[jj]) dma16(ra, a_voff[jj], sA + buf * kStageElems + (wave * L::A_PER_WAVE + jj) * 512);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) dma16(rb, b_voff[jj], sB + buf * kStageElems + (wave * 4 + jj) * 512);
+  };
+
+  // ---- fragment read offsets (bytes, relative to a stage) ------------------------
+  const int l31 = lane & 31;
+  uint32_t a_rd[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int row = wm * (MI * 32) + l31;
+    const int c = (2 * kk + (lane >> 5)) ^ ((l31 >> 2) & 3);
+    a_rd[kk] = static_cast<uint32_t>(row * kBK + c * 8) * 2u;
+  }
+  auto bcol = [&](int ni) {
+    constexpr int half = NI / 2;
+    if (SWIGLU) return ni < half ? wn * (128 / WN) + ni * 32 : 128 + wn * (128 / WN) + (ni - half) * 32;
+    return wn * (256 / WN) + ni * 32;
+  };
+  uint32_t b_rd[NI];
+  {
+    const int g = lane >> 4, i = lane & 15;
+    const int kl = (g >> 1) * 8 + (i >> 2);
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int n = bcol(ni) + (g & 1) * 16 + 4 * (i & 3);
+      b_rd[ni] = static_cast<uint32_t>(kl * 256 + (((n >> 3) ^ (4 * (kl & 3))) * 8) + (n & 4)) * 2u;
+    }
+  }
+  const uint32_t sA_addr = lds_addr(sA), sB_addr = lds_addr(sB);
+
+  auto read_frags = [&](Frags& f, int buf, int kk) {
+    const uint32_t ab = sA_addr + buf * kStageBytes + a_rd[kk];
+    const uint32_t bb = sB_addr + buf * kStageBytes;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      if (mi == 0) f.a[0] = ds_read16<0>(ab);
+      if (mi == 1) f.a[1] = ds_read16<2048>(ab);
+      if (mi == 2) f.a[2] = ds_read16<4096>(ab);
+      if (mi == 3) f.a[3] = ds_read16<6144>(ab);
+    }
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const uint32_t bn = bb + b_rd[ni];
+      if (kk == 0) {
+        f.b[ni][0] = ds_read_tr<0>(bn);
+        f.b[ni][1] = ds_read_tr<2048>(bn);
+      } else {
+        f.b[ni][0] = ds_read_tr<8192>(bn);
+        f.b[ni][1] = ds_read_tr<10240>(bn);
+      }
+    }
+  };
+  auto tie_frags = [&](Frags& f) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) tie(f.a[mi]);
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      tie(f.b[ni][0]);
+      tie(f.b[ni][1]);
+    }
+  };
+
+  f32x16_t acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+
+  auto mfmas = [&](const Frags& f) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const i16x8_t b = __builtin_shufflevector(f.b[ni][0], f.b[ni][1], 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], __builtin_bit_cast(bf16x8_t, b),
+                                                              acc[mi][ni], 0, 0, 0);
+      }
+  };
+
+  // ---- pipeline ---------------------------------------------------------------------
+  // outstanding DMA stages after stage s has landed: min(kStages - 2, ksteps - 1 - s)
+  auto wait_stage = [&](int s) {
+    const int after = min(kStages - 2, ksteps - 1 - s);
+    wait_vmcnt(after * per_stage);
+  };
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s)
+    if (s < ksteps) issue(s);
+  wait_stage(0);
+  __builtin_amdgcn_s_barrier();
+  if (kStages - 1 < ksteps) issue(kStages - 1);
+  Frags f0, f1;
+  read_frags(f0, 0, 0);
+
+  for (int ks = 0; ks < ksteps; ++ks) {
+    const int buf = ks % kStages;
+    read_frags(f1, buf, 1);
+    wait_lgkmcnt<L::LDS_READS>();
+    tie_frags(f0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(f0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_lgkmcnt<0>();
+    tie_frags(f1);
+    if (ks + 1 < ksteps) {
+      wait_stage(ks + 1);
+      __builtin_amdgcn_s_barrier();  // stage ks+1 landed everywhere; stage ks is no longer read
+      if (ks + kStages < ksteps) issue(ks + kStages);
+      read_frags(f0, (ks + 1) % kStages, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(f1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // ---- epilogue (as in the register-staged kernel) -------------------------------------
+  const __amdgpu_buffer_rsrc_t rc_src = make_rsrc(
+      C + static_cast<int64_t>(row0) * N, static_cast<uint32_t>(rows_valid) * static_cast<uint32_t>(N) * 2u);
+  constexpr int kStoreBlocks = SWIGLU ? NI / 2 : NI;
+  uint32_t col_off[kStoreBlocks];
+#pragma unroll
+  for (int ni = 0; ni < kStoreBlocks; ++ni) {
+    const int col = n0 + (SWIGLU ? wn * (128 / WN) : wn * (256 / WN)) + ni * 32 + l31;
+    col_off[ni] = col < N ? static_cast<uint32_t>(col) * 2u : 0x80000000u;
+  }
+  const uint32_t c_row_bytes = static_cast<uint32_t>(N) * 2u;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = wm * (MI * 32) + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+      const uint32_t row_off = static_cast<uint32_t>(row) * c_row_bytes;
+#pragma unroll
+      for (int ni = 0; ni < kStoreBlocks; ++ni) {
+        const float v = SWIGLU ? silu_fast(acc[mi][ni][r]) * acc[mi][ni + NI / 2][r] : acc[mi][ni][r];
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(v), rc_src, static_cast<int>(row_off + col_off[ni]),
+                                              0, 0);
+      }
+    }
+  }
+}
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_lds_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
+    const int32_t* __restrict__ offsets, int e_begin, int e_loc, int K, int N, int ldb, int n_max) {
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * kStages * kStageElems];
+  __shared__ TileMap tm;
+  build_tile_map<256>(tm, offsets, e_begin, e_loc, n_max);
+
+  constexpr int kOutCols = SWIGLU ? 128 : 256;
+  const int n_tiles = (N + kOutCols - 1) / kOutCols;
+  const int total = uniform(tm.mstart[e_loc]) * n_tiles;
+  const int64_t b_expert = static_cast<int64_t>(K) * ldb;
+
+  for (int tile = xcd_remap(blockIdx.x, gridDim.x); tile < total; tile += gridDim.x) {
+    const TileCoord tc = find_tile(tm, tile, n_tiles, e_loc);
+    const int row0 = uniform(tm.rstart[tc.e]) + tc.mt * 256;
+    const int rows_valid = min(256, uniform(tm.rstart[tc.e + 1]) - row0);
+    const int n0 = tc.nt * kOutCols;
+    const uint16_t* Bexp = B + static_cast<int64_t>(tc.e) * b_expert;
+    if (rows_valid > 128)
+      gemm_tile<SWIGLU, 256>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb);
+    else if (rows_valid > 64)
+      gemm_tile<SWIGLU, 128>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb);
+    else if (rows_valid > 32)
+      gemm_tile<SWIGLU, 64>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb);
+    else
+      gemm_tile<SWIGLU, 32>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb);
+    // every wave has waited for its last LDS reads; the next tile's loads may land
+    __builtin_amdgcn_s_barrier();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_grouped_gemm_lds(const void* x_perm, const int32_t* offsets, const void* w_gu,
+                                   const void* w_dn, void* h, void* y, int d, int d_ff, int e_begin,
+                                   int e_loc, int64_t n_max, int grid_gate_up, int grid_down,
+                                   hipStream_t stream) {
+  hipLaunchKernelGGL(grouped_gemm_lds_kernel<true>, dim3(grid_gate_up), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(x_perm), static_cast<const uint16_t*>(w_gu),
+                     static_cast<uint16_t*>(h), offsets, e_begin, e_loc, d, d_ff, 2 * d_ff,
+                     static_cast<int>(n_max));
+  hipLaunchKernelGGL(grouped_gemm_lds_kernel<false>, dim3(grid_down), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_dn),
+                     static_cast<uint16_t*>(y), offsets, e_begin, e_loc, d_ff, d, d, static_cast<int>(n_max));
+  return hipGetLastError();
+}
+
+}  // namespace moe

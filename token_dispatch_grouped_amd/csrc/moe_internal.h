@@ -44,6 +44,10 @@ hipError_t launch_grouped_gemm_bf16(const void* x_perm, const int32_t* offsets, 
                                     const void* w_dn, void* h, void* y, int d, int d_ff, int e_begin,
                                     int e_loc, int64_t n_max, int64_t T, int k, int E,
                                     hipStream_t stream);
+hipError_t launch_grouped_gemm_lds(const void* x_perm, const int32_t* offsets, const void* w_gu,
+                                   const void* w_dn, void* h, void* y, int d, int d_ff, int e_begin,
+                                   int e_loc, int64_t n_max, int grid_gate_up, int grid_down,
+                                   hipStream_t stream);
 hipError_t launch_grouped_gemm_f32(const float* x_perm, const int32_t* offsets, const float* w_gu,
                                    const float* w_dn, float* h, float* y, int d, int d_ff,
                                    int e_begin, int e_loc, int64_t n_max, hipStream_t stream);
