@@ -238,8 +238,9 @@ def _one_hot_logits(counts, E, seed):
 
 
 def test_layer_every_tile_height():
-    """Experts whose row counts hit every tail-tile height (32/64/128/256) and the edges."""
-    counts = [0, 1, 31, 32, 33, 64, 65, 128, 129, 255, 256, 257, 300, 513]
+    """Experts whose row counts hit every row-tile height (32/64/128/256, and 256 plus a
+    merged tail of up to 32 rows) and the edges between them."""
+    counts = [0, 1, 31, 32, 33, 64, 65, 128, 129, 255, 256, 257, 288, 289, 300, 513, 544]
     E = len(counts)
     w = mi.Workload("tile_heights", int(sum(counts)), 256, 160, E, 1, 0, E, "bf16", 23)
     res, ref = _layer_case(w, _one_hot_logits(counts, E, 23))

@@ -21,7 +21,19 @@ struct TileMap {
 // Rows are clamped to [0, n_max): with a caller-supplied topk_idx that repeats an
 // id inside a token, local pairs could exceed n_max; those rows are dropped
 // rather than written past the end of H and Y.
-template <int BM>
+//
+// Row tiles of an expert with R rows: BM-row tiles, and the remainder R % BM as
+// one more, shorter tile -- unless MERGE_TAIL > 0, the remainder is at most
+// MERGE_TAIL rows and there is a full tile to absorb it, in which case the
+// last full tile grows to BM + remainder rows instead.
+template <int BM, int MERGE_TAIL = 0>
+__device__ __forceinline__ int row_tiles(int rows) {
+  const int full = rows / BM, rem = rows % BM;
+  if (MERGE_TAIL > 0 && full > 0 && rem <= MERGE_TAIL) return full;
+  return full + (rem > 0);
+}
+
+template <int BM, int MERGE_TAIL = 0>
 __device__ void build_tile_map(TileMap& tm, const int32_t* __restrict__ offsets, int e_begin,
                                int e_loc, int n_max) {
   if (threadIdx.x < kWave) {
@@ -35,7 +47,7 @@ __device__ void build_tile_map(TileMap& tm, const int32_t* __restrict__ offsets,
         start = min(offsets[e_begin + e] - base, n_max);
         rows = min(offsets[e_begin + e + 1] - base, n_max) - start;
       }
-      const int mt = (rows + BM - 1) / BM;
+      const int mt = row_tiles<BM, MERGE_TAIL>(rows);
       int incl = mt;
 #pragma unroll
       for (int off = 1; off < kWave; off <<= 1) {

@@ -31,6 +31,8 @@
 //     H >= 64, 1 x 4 waves of 32 x 64 for H = 32.
 //   * Tile walk, XCD mapping and the buffer-store epilogue follow the
 //     register-staged kernel.
+#include <type_traits>
+
 #include "gemm_common.h"
 
 namespace moe {
@@ -43,36 +45,41 @@ using namespace gemm;
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x8_t __attribute__((ext_vector_type(8)));
 
-constexpr int kBK = 32;                      // K per stage
+constexpr int kBK = 32;                       // K per stage
 constexpr int kStages = 4;
-constexpr int kStageElems = 256 * kBK;       // bf16 per operand per stage (16 KB)
-constexpr uint32_t kStageBytes = kStageElems * 2;
+constexpr int kARows = 256;                   // rows an activation stage holds
+constexpr int kAStageElems = kARows * kBK;    // 18 KB
+constexpr int kBStageElems = 256 * kBK;       // 16 KB
+constexpr uint32_t kAStageBytes = kAStageElems * 2;
+constexpr uint32_t kBStageBytes = kBStageElems * 2;
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const LDS3 char*)p));
 }
 
-// Wait until at most n vector-memory operations of this wave are outstanding
-// (n is wave-uniform; rounded down to a count this kernel uses, which only waits longer).
-__device__ __forceinline__ void wait_vmcnt(int n) {
-  if (n >= 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else if (n >= 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-  else if (n >= 10) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-  else if (n >= 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else if (n >= 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-  else if (n >= 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-  else if (n >= 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+// s_waitcnt with a compile-time count (the counts this kernel uses).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (N == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+  else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+  else if constexpr (N == 10) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+  else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if constexpr (N == 18) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+  else static_assert(N == 0, "add the count");
 }
 
 template <int N>
 __device__ __forceinline__ void wait_lgkmcnt() {
-  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
   if constexpr (N == 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   else if constexpr (N == 5) asm volatile("s_waitcnt lgkmcnt(5)" ::: "memory");
   else if constexpr (N == 9) asm volatile("s_waitcnt lgkmcnt(9)" ::: "memory");
   else if constexpr (N == 10) asm volatile("s_waitcnt lgkmcnt(10)" ::: "memory");
   else if constexpr (N == 12) asm volatile("s_waitcnt lgkmcnt(12)" ::: "memory");
+  else if constexpr (N == 13) asm volatile("s_waitcnt lgkmcnt(13)" ::: "memory");
   else static_assert(N == 0, "add the count");
 }
 
@@ -95,25 +102,36 @@ __device__ __forceinline__ i16x4_t ds_read_tr(uint32_t addr) {
   return v;
 }
 
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, void* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS3 void*)lds, 16, voff, 0, 0, 0);
+// 16 bytes per lane from the buffer into LDS at lds_base + 16 * lane (lds_base is
+// a wave-uniform LDS byte address).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS3 void*)(uintptr_t)lds_base, 16, voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8_t join(i16x4_t lo, i16x4_t hi) {
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 struct Frags {
-  // up to 4 A blocks and 4 B blocks (each B block = two 4-k halves)
-  bf16x8_t a[4];
-  i16x4_t b[4][2];
+  bf16x8_t a[4];   // A blocks (32 rows each)
+  bf16x8_t ax;     // the extra 32-row A block of a 288-row tile
+  i16x4_t b[4][2]; // B blocks (32 columns each), two 4-k halves
 };
 
+// H = rows of the tile: 32, 64, 128, 256, or 288 (256 + a merged tail of <= 32).
 template <int H>
 struct Layout {
-  static constexpr int WM = H >= 64 ? 2 : 1;       // waves along M
+  static constexpr bool EXTRA = H > 256;
+  static constexpr int HM = EXTRA ? 256 : H;       // rows on the regular wave grid
+  static constexpr int WM = HM >= 64 ? 2 : 1;      // waves along M
   static constexpr int WN = 4 / WM;                // waves along N
-  static constexpr int MI = H / WM / 32;           // 32-row MFMA blocks per wave
+  static constexpr int MI = HM / WM / 32;          // 32-row MFMA blocks per wave
   static constexpr int NI = 256 / WN / 32;         // 32-column MFMA blocks per wave
-  static constexpr int A_INSTR = H / 16;           // 1 KB DMA instructions per A stage
-  static constexpr int A_PER_WAVE = A_INSTR >= 4 ? A_INSTR / 4 : 1;
-  static constexpr int LDS_READS = MI + 2 * NI;    // LDS instructions per 16-wide K slice
+  static constexpr int A_INSTR = H / 16;           // 1 KB DMA instructions per activation stage
+  static constexpr int A_PER_WAVE = (A_INSTR + 3) / 4;
+  static constexpr int PER = 4 + A_PER_WAVE;       // DMA instructions per stage per wave
+  static constexpr int LDS_READS = MI + 2 * NI + (EXTRA ? 1 : 0);
+  static constexpr int NMFMA = MI * NI;            // regular MFMAs per 16-wide K slice
 };
 
 template <bool SWIGLU, int H>
@@ -121,30 +139,36 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
                                           const uint16_t* __restrict__ Bexp, uint16_t* __restrict__ C,
                                           int row0, int rows_valid, int n0, int K, int N, int ldb) {
   using L = Layout<H>;
-  constexpr int MI = L::MI, NI = L::NI, WN = L::WN;
+  constexpr int MI = L::MI, NI = L::NI, WM = L::WM, WN = L::WN, PER = L::PER;
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = uniform(tid / kWave);
   const int wm = wave / WN, wn = wave % WN;
   const int ksteps = K / kBK;
 
-  uint16_t* sA = smem;
-  uint16_t* sB = smem + kStages * kStageElems;
+  const uint32_t sA_base = uniform(static_cast<int>(lds_addr(smem)));
+  const uint32_t sB_base = sA_base + kStages * kAStageBytes;
 
-  // ---- DMA issue: per-lane byte offsets (constant over the tile) ----------------
+  // ---- DMA: per-lane byte offsets, constant over the tile ---------------------------
+  // Activation instruction j covers rows 16j..16j+15: lane L brings row 16j + L/4,
+  // logical chunk (L & 3) ^ ((row >> 2) & 3) into LDS slot L. Slots beyond the
+  // A_INSTR instructions repeat an earlier instruction (identical bytes to the same
+  // place), so every wave issues PER loads per stage.
   const uint16_t* a_tile = A + static_cast<int64_t>(row0) * K;
   const uint32_t a_bytes = static_cast<uint32_t>(rows_valid) * static_cast<uint32_t>(K) * 2u;
   const uint32_t b_bytes = static_cast<uint32_t>(K) * static_cast<uint32_t>(ldb) * 2u;
   uint32_t a_voff[L::A_PER_WAVE];
-  bool a_on[L::A_PER_WAVE];
+  int a_slot[L::A_PER_WAVE];
 #pragma unroll
   for (int jj = 0; jj < L::A_PER_WAVE; ++jj) {
-    const int j = wave * L::A_PER_WAVE + jj;
-    a_on[jj] = j < L::A_INSTR;
+    const int j = (wave * L::A_PER_WAVE + jj) % L::A_INSTR;
+    a_slot[jj] = j;
     const int r = 16 * j + (lane >> 2);
     const int c = (lane & 3) ^ ((lane >> 4) & 3);
     a_voff[jj] = static_cast<uint32_t>(r) * static_cast<uint32_t>(K) * 2u + static_cast<uint32_t>(c) * 16u;
   }
+  // Weight instruction j covers k-rows 2j, 2j+1 of the stage: lane L brings k-row
+  // 2j + L/32, logical chunk (L & 31) ^ (4 * (k & 3)) (8 columns) into LDS slot L.
   uint32_t b_voff[4];
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
@@ -156,21 +180,21 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
     else col = n0 + 8 * c;
     b_voff[jj] = (static_cast<uint32_t>(kl) * static_cast<uint32_t>(ldb) + static_cast<uint32_t>(col)) * 2u;
   }
-  const int per_stage = 4 + (a_on[0] ? L::A_PER_WAVE : 0);
 
   auto issue = [&](int s) {
     const int buf = s % kStages;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_tile + s * kBK, a_bytes - static_cast<uint32_t>(s) * kBK * 2u);
-    const __amdgpu_buffer_rsrc_t rb =
-        make_rsrc(Bexp + static_cast<int64_t>(s) * kBK * ldb, b_bytes - static_cast<uint32_t>(s) * kBK * ldb * 2u);
+    const __amdgpu_buffer_rsrc_t ra =
+        make_rsrc(a_tile + s * kBK, a_bytes - static_cast<uint32_t>(s) * kBK * 2u);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bexp + static_cast<int64_t>(s) * kBK * ldb,
+                                                b_bytes - static_cast<uint32_t>(s) * kBK * ldb * 2u);
 #pragma unroll
     for (int jj = 0; jj < L::A_PER_WAVE; ++jj)
-      if (a_on[jj]) dma16(ra, a_voff[jj], sA + buf * kStageElems + (wave * L::A_PER_WAVE + jj) * 512);
+      dma16(ra, a_voff[jj], sA_base + buf * kAStageBytes + a_slot[jj] * 1024);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) dma16(rb, b_voff[jj], sB + buf * kStageElems + (wave * 4 + jj) * 512);
+    for (int jj = 0; jj < 4; ++jj) dma16(rb, b_voff[jj], sB_base + buf * kBStageBytes + (wave * 4 + jj) * 1024);
   };
 
-  // ---- fragment read offsets (bytes, relative to a stage) ------------------------
+  // ---- fragment reads ----------------------------------------------------------------
   const int l31 = lane & 31;
   uint32_t a_rd[2];
 #pragma unroll
@@ -179,10 +203,22 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
     const int c = (2 * kk + (lane >> 5)) ^ ((l31 >> 2) & 3);
     a_rd[kk] = static_cast<uint32_t>(row * kBK + c * 8) * 2u;
   }
+  // B-tile column of register slot ni. With two wave rows, slot order is
+  // rotated by wm so that slots 0 and (SwiGLU) 2 / (plain) 1 are the columns
+  // this wave also covers for the extra 32-row block of a 288-row tile.
   auto bcol = [&](int ni) {
-    constexpr int half = NI / 2;
-    if (SWIGLU) return ni < half ? wn * (128 / WN) + ni * 32 : 128 + wn * (128 / WN) + (ni - half) * 32;
-    return wn * (256 / WN) + ni * 32;
+    if constexpr (WM == 2) {
+      if (SWIGLU) {
+        const int sub = (ni & 1) ^ wm;  // which 32-wide half of the wave's 64 gate columns
+        return (ni < 2 ? 0 : 128) + wn * 64 + sub * 32;
+      }
+      const int blk = (ni + 2 * wm) & 3;
+      return wn * 128 + blk * 32;
+    } else {
+      constexpr int half = NI / 2;
+      if (SWIGLU) return ni < half ? wn * (128 / WN) + ni * 32 : 128 + wn * (128 / WN) + (ni - half) * 32;
+      return wn * (256 / WN) + ni * 32;
+    }
   };
   uint32_t b_rd[NI];
   {
@@ -194,17 +230,18 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
       b_rd[ni] = static_cast<uint32_t>(kl * 256 + (((n >> 3) ^ (4 * (kl & 3))) * 8) + (n & 4)) * 2u;
     }
   }
-  const uint32_t sA_addr = lds_addr(sA), sB_addr = lds_addr(sB);
+  const uint32_t sA_addr = sA_base, sB_addr = sB_base;
 
   auto read_frags = [&](Frags& f, int buf, int kk) {
-    const uint32_t ab = sA_addr + buf * kStageBytes + a_rd[kk];
-    const uint32_t bb = sB_addr + buf * kStageBytes;
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      if (mi == 0) f.a[0] = ds_read16<0>(ab);
-      if (mi == 1) f.a[1] = ds_read16<2048>(ab);
-      if (mi == 2) f.a[2] = ds_read16<4096>(ab);
-      if (mi == 3) f.a[3] = ds_read16<6144>(ab);
+    const uint32_t ab = sA_addr + buf * kAStageBytes + a_rd[kk];
+    const uint32_t bb = sB_addr + buf * kBStageBytes;
+    if constexpr (MI > 0) f.a[0] = ds_read16<0>(ab);
+    if constexpr (MI > 1) f.a[1] = ds_read16<2048>(ab);
+    if constexpr (MI > 2) f.a[2] = ds_read16<4096>(ab);
+    if constexpr (MI > 3) f.a[3] = ds_read16<6144>(ab);
+    if constexpr (L::EXTRA) {
+      // rows 256..287: the wave-row offset wm*128 is taken back out
+      f.ax = ds_read16<16384>(ab - static_cast<uint32_t>(wm * 128 * kBK * 2));
     }
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
@@ -221,6 +258,7 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
   auto tie_frags = [&](Frags& f) {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) tie(f.a[mi]);
+    if constexpr (L::EXTRA) tie(f.ax);
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
       tie(f.b[ni][0]);
@@ -229,29 +267,47 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
   };
 
   f32x16_t acc[MI][NI];
+  f32x16_t accx[2];
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) accx[0][r] = accx[1][r] = 0.f;
 
-  auto mfmas = [&](const Frags& f) {
+  // MFMAs with flat block index in [LO, HI) (row-major over mi, ni); the extra
+  // block's two MFMAs go with the second part.
+  auto mfmas = [&](const Frags& f, auto lo_c, auto hi_c, auto extra_c) {
+    constexpr int LO = decltype(lo_c)::value, HI = decltype(hi_c)::value;
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        const i16x8_t b = __builtin_shufflevector(f.b[ni][0], f.b[ni][1], 0, 1, 2, 3, 4, 5, 6, 7);
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], __builtin_bit_cast(bf16x8_t, b),
-                                                              acc[mi][ni], 0, 0, 0);
-      }
+    for (int q = LO; q < HI; ++q) {
+      const int mi = q / NI, ni = q % NI;
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], join(f.b[ni][0], f.b[ni][1]), acc[mi][ni],
+                                                            0, 0, 0);
+    }
+    if constexpr (L::EXTRA && decltype(extra_c)::value) {
+      constexpr int s1 = SWIGLU ? 2 : 1;
+      accx[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.ax, join(f.b[0][0], f.b[0][1]), accx[0], 0, 0, 0);
+      accx[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.ax, join(f.b[s1][0], f.b[s1][1]), accx[1], 0, 0, 0);
+    }
   };
+  using Z = std::integral_constant<int, 0>;
+  using Half = std::integral_constant<int, L::NMFMA / 2>;
+  using All = std::integral_constant<int, L::NMFMA>;
+  using No = std::integral_constant<bool, false>;
+  using Yes = std::integral_constant<bool, true>;
 
-  // ---- pipeline ---------------------------------------------------------------------
-  // outstanding DMA stages after stage s has landed: min(kStages - 2, ksteps - 1 - s)
+  // ---- pipeline -------------------------------------------------------------------------
+  // Stage s lands in buffer s % kStages; it is issued three stages ahead. When a
+  // wave waits for stage s, min(kStages - 2, ksteps - 1 - s) later stages of its
+  // own loads may still be in flight.
   auto wait_stage = [&](int s) {
     const int after = min(kStages - 2, ksteps - 1 - s);
-    wait_vmcnt(after * per_stage);
+    if (after >= 2) wait_vmcnt<2 * PER>();
+    else if (after == 1) wait_vmcnt<PER>();
+    else wait_vmcnt<0>();
   };
 #pragma unroll
   for (int s = 0; s < kStages - 1; ++s)
@@ -264,36 +320,63 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
 
   for (int ks = 0; ks < ksteps; ++ks) {
     const int buf = ks % kStages;
+    if constexpr (L::EXTRA) {
+      // 288-row tiles keep one fragment set (the extra block's accumulators
+      // take the registers of the second): read, wait, multiply, per slice.
+      wait_lgkmcnt<0>();
+      tie_frags(f0);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(f0, Z{}, All{}, Yes{});
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(f0, buf, 1);
+      wait_lgkmcnt<0>();  // this wave's reads of stage ks are complete
+      tie_frags(f0);
+      if (ks + 1 < ksteps) {
+        wait_stage(ks + 1);
+        __builtin_amdgcn_s_barrier();
+        if (ks + kStages < ksteps) issue(ks + kStages);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(f0, Z{}, All{}, Yes{});
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks + 1 < ksteps) read_frags(f0, (ks + 1) % kStages, 0);
+      continue;
+    }
     read_frags(f1, buf, 1);
     wait_lgkmcnt<L::LDS_READS>();
     tie_frags(f0);
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(f0);
+    mfmas(f0, Z{}, Half{}, No{});
     __builtin_amdgcn_sched_barrier(0);
-    wait_lgkmcnt<0>();
+    wait_lgkmcnt<0>();  // this wave's reads of stage ks are complete
     tie_frags(f1);
     if (ks + 1 < ksteps) {
       wait_stage(ks + 1);
-      __builtin_amdgcn_s_barrier();  // stage ks+1 landed everywhere; stage ks is no longer read
+      __builtin_amdgcn_s_barrier();  // stage ks+1 landed for every wave; nobody reads stage ks any more
       if (ks + kStages < ksteps) issue(ks + kStages);
-      read_frags(f0, (ks + 1) % kStages, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(f1);
+    mfmas(f0, Half{}, All{}, Yes{});
+    __builtin_amdgcn_sched_barrier(0);
+    // the next stage's first slice is read while this slice's MFMAs run
+    if (ks + 1 < ksteps) read_frags(f0, (ks + 1) % kStages, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(f1, Z{}, All{}, Yes{});
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- epilogue (as in the register-staged kernel) -------------------------------------
+  // ---- epilogue: bf16 results through buffer stores over the tile's valid rows --------
   const __amdgpu_buffer_rsrc_t rc_src = make_rsrc(
       C + static_cast<int64_t>(row0) * N, static_cast<uint32_t>(rows_valid) * static_cast<uint32_t>(N) * 2u);
-  constexpr int kStoreBlocks = SWIGLU ? NI / 2 : NI;
-  uint32_t col_off[kStoreBlocks];
-#pragma unroll
-  for (int ni = 0; ni < kStoreBlocks; ++ni) {
-    const int col = n0 + (SWIGLU ? wn * (128 / WN) : wn * (256 / WN)) + ni * 32 + l31;
-    col_off[ni] = col < N ? static_cast<uint32_t>(col) * 2u : 0x80000000u;
-  }
   const uint32_t c_row_bytes = static_cast<uint32_t>(N) * 2u;
+  auto col_off = [&](int ni) -> uint32_t {  // output column of register slot ni (gate slot for SwiGLU)
+    const int col = n0 + bcol(ni) + l31;
+    return col < N ? static_cast<uint32_t>(col) * 2u : 0x80000000u;
+  };
+  constexpr int kStoreBlocks = SWIGLU ? NI / 2 : NI;
+  uint32_t coff[kStoreBlocks];
+#pragma unroll
+  for (int ni = 0; ni < kStoreBlocks; ++ni) coff[ni] = col_off(ni);
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
@@ -303,7 +386,25 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
 #pragma unroll
       for (int ni = 0; ni < kStoreBlocks; ++ni) {
         const float v = SWIGLU ? silu_fast(acc[mi][ni][r]) * acc[mi][ni + NI / 2][r] : acc[mi][ni][r];
-        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(v), rc_src, static_cast<int>(row_off + col_off[ni]),
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(v), rc_src, static_cast<int>(row_off + coff[ni]), 0,
+                                              0);
+      }
+    }
+  }
+  if constexpr (L::EXTRA) {
+    const uint32_t cx0 = coff[0];
+    const uint32_t cx1 = SWIGLU ? 0u : coff[1];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 256 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+      const uint32_t row_off = static_cast<uint32_t>(row) * c_row_bytes;
+      if (SWIGLU) {
+        const float v = silu_fast(accx[0][r]) * accx[1][r];
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(v), rc_src, static_cast<int>(row_off + cx0), 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(accx[0][r]), rc_src, static_cast<int>(row_off + cx0),
+                                              0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(accx[1][r]), rc_src, static_cast<int>(row_off + cx1),
                                               0, 0);
       }
     }
@@ -314,7 +415,7 @@ template <bool SWIGLU>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_lds_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
     const int32_t* __restrict__ offsets, int e_begin, int e_loc, int K, int N, int ldb, int n_max) {
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * kStages * kStageElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[kStages * (kAStageElems + kBStageElems)];
   __shared__ TileMap tm;
   build_tile_map<256>(tm, offsets, e_begin, e_loc, n_max);
 
@@ -326,7 +427,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_lds_kernel(
   for (int tile = xcd_remap(blockIdx.x, gridDim.x); tile < total; tile += gridDim.x) {
     const TileCoord tc = find_tile(tm, tile, n_tiles, e_loc);
     const int row0 = uniform(tm.rstart[tc.e]) + tc.mt * 256;
-    const int rows_valid = min(256, uniform(tm.rstart[tc.e + 1]) - row0);
+    const int row_end = uniform(tm.rstart[tc.e + 1]);
+    const int mt_e = uniform(tm.mstart[tc.e + 1]) - uniform(tm.mstart[tc.e]);
+    const int rows_valid = tc.mt == mt_e - 1 ? row_end - row0 : 256;
     const int n0 = tc.nt * kOutCols;
     const uint16_t* Bexp = B + static_cast<int64_t>(tc.e) * b_expert;
     if (rows_valid > 128)
