@@ -7,9 +7,10 @@
 // the token's local pairs, in slot order, in fp32; zero if it has none.
 //
 // Design: one wave per token (grid-stride). The token's k row indices and
-// weights are wave-uniform scalar loads; each lane owns 16-byte column chunks
-// and keeps kChunks of them in flight per slot, so a token issues k * kChunks
-// independent 16-byte loads per lane. HBM-bound: N_loc*d*b read + T*d*b written.
+// weights come in with one vector load (a lane per slot); a ballot gives the
+// local slots, visited in slot order through readlane, and a token with none
+// writes its zero row directly. Each lane owns 16-byte column chunks and keeps
+// kChunks of them in flight per slot. HBM-bound: N_loc*d*b read + T*d*b written.
 #include "moe_internal.h"
 
 namespace moe {
@@ -66,34 +67,53 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint4* __restri
   using V = Vec<BF16>;
   const int lane = lane_id();
   const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kThreads / kWave);
-  for (int64_t t = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave; t < T;
+  for (int64_t t = uniform(static_cast<int>(blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave)); t < T;
        t += nwaves) {
+    // slots j0..j0+63 of this token, one per lane; local ones are visited in slot order
+    const int64_t pbase = t * k;
+    bool any = false;
+    for (int j0 = 0; j0 < k; j0 += kWave) {
+      const int j = j0 + lane;
+      const int r = j < k ? pair_pos[pbase + j] : -1;
+      any = any || __ballot(r >= 0 && r < n_max) != 0;
+    }
+    uint4* dst = out + t * row_vec;
+    if (!any) {
+      for (int c = lane; c < row_vec; c += kWave) dst[c] = make_uint4(0, 0, 0, 0);
+      continue;
+    }
     for (int c0 = 0; c0 < row_vec; c0 += kChunks * kWave) {
       float acc[kChunks][V::kN];
 #pragma unroll
       for (int q = 0; q < kChunks; ++q)
 #pragma unroll
         for (int i = 0; i < V::kN; ++i) acc[q][i] = 0.f;
-      for (int j = 0; j < k; ++j) {
-        const int r = pair_pos[t * k + j];
-        if (r < 0 || r >= n_max) continue;
-        const float wj = w[t * k + j];
-        const uint4* src = y + static_cast<int64_t>(r) * row_vec;
-        uint4 v[kChunks];
+      for (int j0 = 0; j0 < k; j0 += kWave) {
+        const int j = j0 + lane;
+        const int rl = j < k ? pair_pos[pbase + j] : -1;
+        const float wl = j < k ? w[pbase + j] : 0.f;
+        uint64_t mask = __ballot(rl >= 0 && rl < n_max);
+        while (mask) {
+          const int src = __ffsll(static_cast<unsigned long long>(mask)) - 1;
+          mask &= mask - 1;
+          const int r = __builtin_amdgcn_readlane(rl, src);
+          const float wj = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wl), src));
+          const uint4* row = y + static_cast<int64_t>(r) * row_vec;
+          uint4 v[kChunks];
 #pragma unroll
-        for (int q = 0; q < kChunks; ++q) {
-          const int c = c0 + q * kWave + lane;
-          v[q] = c < row_vec ? src[c] : make_uint4(0, 0, 0, 0);
-        }
+          for (int q = 0; q < kChunks; ++q) {
+            const int c = c0 + q * kWave + lane;
+            v[q] = c < row_vec ? row[c] : make_uint4(0, 0, 0, 0);
+          }
 #pragma unroll
-        for (int q = 0; q < kChunks; ++q) {
-          float f[V::kN];
-          V::load(v[q], f);
+          for (int q = 0; q < kChunks; ++q) {
+            float f[V::kN];
+            V::load(v[q], f);
 #pragma unroll
-          for (int i = 0; i < V::kN; ++i) acc[q][i] = fmaf(wj, f[i], acc[q][i]);
+            for (int i = 0; i < V::kN; ++i) acc[q][i] = fmaf(wj, f[i], acc[q][i]);
+          }
         }
       }
-      uint4* dst = out + t * row_vec;
 #pragma unroll
       for (int q = 0; q < kChunks; ++q) {
         const int c = c0 + q * kWave + lane;

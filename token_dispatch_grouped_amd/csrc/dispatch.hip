@@ -10,10 +10,11 @@
 // Design (four small launches, all bounded by the pair count or HBM):
 //   1. count   : one workgroup per chunk of kDispatchChunk flat pairs builds an
 //                LDS histogram and stores it expert-major: ws[e * n_chunks + c].
-//   2. scan    : one workgroup scans ws in place (exclusive, expert-major). Entry
-//                (e, c) becomes the first sorted slot of chunk c's pairs of
-//                expert e; counts and offsets fall out of the same scan.
-//   3. scatter : each chunk walks its pairs in order, 256 at a time. A wave
+//   2. scan    : one workgroup, one wave per expert, scans the histogram in
+//                expert-major order: counts, offsets, and the first sorted slot
+//                of chunk c's pairs of expert e, stored chunk-major.
+//   3. scatter : each chunk stages its E first slots in LDS and walks its
+//                pairs in order, 256 at a time. A wave
 //                finds the lanes holding the same expert with a ballot loop;
 //                the rank among them is a popcount, and per-wave counts in LDS
 //                order the waves. Slot = chunk base + running count + rank, so
@@ -47,53 +48,79 @@ __global__ __launch_bounds__(kThreads) void dispatch_count_kernel(const int32_t*
 }
 
 constexpr int kScanThreads = 1024;
+constexpr int kScanWaves = kScanThreads / kWave;
 
-__global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(int32_t* __restrict__ ws,
+// Exclusive scan of the (expert, chunk) histogram in expert-major order, one
+// wave per expert: the expert's per-chunk counts are contiguous, read and
+// prefix-summed 64 at a time. Writes counts and offsets, and the first sorted
+// slot of every (chunk, expert) pair chunk-major, base[c * E + e], so that a
+// scatter workgroup reads its E bases as one contiguous row.
+__global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(const int32_t* __restrict__ ws,
+                                                                     int32_t* __restrict__ base,
                                                                      int32_t* __restrict__ counts,
                                                                      int32_t* __restrict__ offsets,
                                                                      int E, int n_chunks) {
-  __shared__ int part[kScanThreads];
-  __shared__ int off_s[kMaxExperts + 1];
-  const int tid = threadIdx.x;
-  const int64_t L = static_cast<int64_t>(E) * n_chunks;
-  const int64_t per = (L + kScanThreads - 1) / kScanThreads;
-  const int64_t b = tid * per;
-  const int64_t end = b + per < L ? b + per : L;
-  int s = 0;
-  for (int64_t i = b; i < end; ++i) s += ws[i];
-  part[tid] = s;
+  __shared__ int tot[kMaxExperts + 1];
+  const int lane = lane_id();
+  const int wv = threadIdx.x / kWave;
+  // 1. per-expert totals
+  for (int e = wv; e < E; e += kScanWaves) {
+    const int32_t* row = ws + static_cast<int64_t>(e) * n_chunks;
+    int s = 0;
+    for (int c = lane; c < n_chunks; c += kWave) s += row[c];
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (lane == 0) tot[e] = s;
+  }
   __syncthreads();
-  // Hillis-Steele inclusive scan over the 1024 partial sums
-  for (int off = 1; off < kScanThreads; off <<= 1) {
-    const int v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+  // 2. exclusive scan of the totals (E <= 1024) by wave 0, 64 at a time
+  if (wv == 0) {
+    int carry = 0;
+    for (int e0 = 0; e0 < E; e0 += kWave) {
+      const int e = e0 + lane;
+      const int v = e < E ? tot[e] : 0;
+      int incl = v;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      if (e < E) {
+        offsets[e] = carry + incl - v;
+        counts[e] = v;
+        tot[e] = carry + incl - v;
+      }
+      carry += __shfl(incl, kWave - 1);
+    }
+    if (lane == 0) offsets[E] = carry;
   }
-  int run = part[tid] - s;  // exclusive prefix of this thread's range
-  for (int64_t i = b; i < end; ++i) {
-    const int v = ws[i];
-    if (i % n_chunks == 0) off_s[i / n_chunks] = run;
-    ws[i] = run;
-    run += v;
-  }
-  if (tid == kScanThreads - 1) off_s[E] = part[kScanThreads - 1];
-  if (n_chunks == 0)
-    for (int e = tid; e <= E; e += kScanThreads) off_s[e] = 0;
   __syncthreads();
-  for (int e = tid; e < E; e += kScanThreads) {
-    offsets[e] = off_s[e];
-    counts[e] = off_s[e + 1] - off_s[e];
+  // 3. per-(chunk, expert) bases
+  for (int e = wv; e < E; e += kScanWaves) {
+    const int32_t* row = ws + static_cast<int64_t>(e) * n_chunks;
+    int carry = tot[e];
+    for (int c0 = 0; c0 < n_chunks; c0 += kWave) {
+      const int c = c0 + lane;
+      const int v = c < n_chunks ? row[c] : 0;
+      int incl = v;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      if (c < n_chunks) base[static_cast<int64_t>(c) * E + e] = carry + incl - v;
+      carry += __shfl(incl, kWave - 1);
+    }
   }
-  if (tid == 0) offsets[E] = off_s[E];
 }
 
 __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
-    const int32_t* __restrict__ idx, const int32_t* __restrict__ ws,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ base,
     const int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-    int32_t* __restrict__ pair_pos, int64_t P, int E, int n_chunks, int e_begin, int e_end) {
+    int32_t* __restrict__ pair_pos, int64_t P, int E, int e_begin, int e_end) {
   constexpr int kWaves = kThreads / kWave;
-  __shared__ int run[kMaxExperts];            // pairs of each expert placed so far by this chunk
+  constexpr int kPasses = kDispatchChunk / kThreads;
+  __shared__ int run[kMaxExperts];            // next sorted slot of each expert for this chunk
   __shared__ int wcnt[kWaves][kMaxExperts];   // per-wave counts of the current pass
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -101,19 +128,24 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
   const int chunk = blockIdx.x;
   const int seg0 = offsets[e_begin];
   const uint64_t lt_mask = (uint64_t{1} << lane) - 1;
-  for (int e = tid; e < E; e += kThreads) run[e] = 0;
+  // every pass's expert id is loaded up front so the loads overlap
+  int ids[kPasses];
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int64_t p = static_cast<int64_t>(chunk) * kDispatchChunk + pass * kThreads + tid;
+    ids[pass] = p < P ? idx[p] : -1;
+  }
+  const int32_t* brow = base + static_cast<int64_t>(chunk) * E;
+  for (int e = tid; e < E; e += kThreads) run[e] = brow[e];
 
-  for (int pass = 0; pass < kDispatchChunk / kThreads; ++pass) {
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
     for (int i = tid; i < kWaves * E; i += kThreads) wcnt[i / E][i % E] = 0;
     __syncthreads();
     const int64_t p = static_cast<int64_t>(chunk) * kDispatchChunk + pass * kThreads + tid;
-    int e = -1;
-    bool valid = false;
-    if (p < P) {
-      e = idx[p];
-      valid = static_cast<unsigned>(e) < static_cast<unsigned>(E);
-      if (!valid) pair_pos[p] = -1;
-    }
+    const int e = ids[pass];
+    const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(E);
+    if (p < P && !valid) pair_pos[p] = -1;
     // lanes of this wave holding the same expert (ballot loop over distinct ids)
     uint64_t remaining = __ballot(valid);
     uint64_t peers = 0;
@@ -128,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
     if (valid && rank == 0) wcnt[wv][e] = __popcll(peers);
     __syncthreads();
     if (valid) {
-      int pos = ws[static_cast<int64_t>(e) * n_chunks + chunk] + run[e] + rank;
+      int pos = run[e] + rank;
       for (int w2 = 0; w2 < wv; ++w2) pos += wcnt[w2][e];
       perm[pos] = static_cast<int32_t>(p);
       pair_pos[p] = (e >= e_begin && e < e_end) ? pos - seg0 : -1;
@@ -139,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
       for (int w2 = 0; w2 < kWaves; ++w2) add += wcnt[w2][x];
       run[x] += add;
     }
-    __syncthreads();
+    __syncthreads();  // wcnt is read above before the next pass clears it
   }
 }
 
@@ -173,7 +205,8 @@ __global__ __launch_bounds__(kThreads) void dispatch_gather_kernel(
 size_t dispatch_workspace_bytes(int64_t T, int k, int E) {
   const int64_t P = T * k;
   const int64_t n_chunks = (P + kDispatchChunk - 1) / kDispatchChunk;
-  return static_cast<size_t>(n_chunks * E) * sizeof(int32_t);
+  // per-(expert, chunk) counts, then per-(chunk, expert) first slots
+  return 2 * static_cast<size_t>(n_chunks * E) * sizeof(int32_t);
 }
 
 hipError_t launch_dispatch(const void* x, size_t row_bytes, const int32_t* idx, int32_t* counts,
@@ -187,11 +220,12 @@ hipError_t launch_dispatch(const void* x, size_t row_bytes, const int32_t* idx, 
     hipLaunchKernelGGL(dispatch_count_kernel, dim3(n_chunks), dim3(kThreads), 0, stream, idx, ws, P,
                        E, n_chunks);
   }
-  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, ws, counts,
+  int32_t* bases = ws + static_cast<int64_t>(n_chunks) * E;
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, ws, bases, counts,
                      offsets, E, n_chunks);
   if (n_chunks == 0) return hipGetLastError();
-  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(n_chunks), dim3(kThreads), 0, stream, idx, ws,
-                     offsets, perm, pair_pos, P, E, n_chunks, e_begin, e_end);
+  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(n_chunks), dim3(kThreads), 0, stream, idx, bases,
+                     offsets, perm, pair_pos, P, E, e_begin, e_end);
   const int row_vec = static_cast<int>(row_bytes / 16);
   const int64_t waves_needed = n_max;  // one wave per row at most
   int64_t blocks = (waves_needed + (kThreads / kWave) - 1) / (kThreads / kWave);

@@ -48,7 +48,7 @@ typedef short i16x8_t __attribute__((ext_vector_type(8)));
 constexpr int kBK = 32;                       // K per stage
 constexpr int kStages = 4;
 constexpr int kARows = 256;                   // rows an activation stage holds
-constexpr int kAStageElems = kARows * kBK;    // 18 KB
+constexpr int kAStageElems = kARows * kBK;    // 16 KB
 constexpr int kBStageElems = 256 * kBK;       // 16 KB
 constexpr uint32_t kAStageBytes = kAStageElems * 2;
 constexpr uint32_t kBStageBytes = kBStageElems * 2;
@@ -114,23 +114,20 @@ __device__ __forceinline__ bf16x8_t join(i16x4_t lo, i16x4_t hi) {
 
 struct Frags {
   bf16x8_t a[4];   // A blocks (32 rows each)
-  bf16x8_t ax;     // the extra 32-row A block of a 288-row tile
   i16x4_t b[4][2]; // B blocks (32 columns each), two 4-k halves
 };
 
-// H = rows of the tile: 32, 64, 128, 256, or 288 (256 + a merged tail of <= 32).
+// H = rows of the tile: 32, 64, 128 or 256.
 template <int H>
 struct Layout {
-  static constexpr bool EXTRA = H > 256;
-  static constexpr int HM = EXTRA ? 256 : H;       // rows on the regular wave grid
-  static constexpr int WM = HM >= 64 ? 2 : 1;      // waves along M
+  static constexpr int WM = H >= 64 ? 2 : 1;       // waves along M
   static constexpr int WN = 4 / WM;                // waves along N
-  static constexpr int MI = HM / WM / 32;          // 32-row MFMA blocks per wave
+  static constexpr int MI = H / WM / 32;           // 32-row MFMA blocks per wave
   static constexpr int NI = 256 / WN / 32;         // 32-column MFMA blocks per wave
   static constexpr int A_INSTR = H / 16;           // 1 KB DMA instructions per activation stage
   static constexpr int A_PER_WAVE = (A_INSTR + 3) / 4;
   static constexpr int PER = 4 + A_PER_WAVE;       // DMA instructions per stage per wave
-  static constexpr int LDS_READS = MI + 2 * NI + (EXTRA ? 1 : 0);
+  static constexpr int LDS_READS = MI + 2 * NI;
   static constexpr int NMFMA = MI * NI;            // regular MFMAs per 16-wide K slice
 };
 
@@ -203,22 +200,12 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
     const int c = (2 * kk + (lane >> 5)) ^ ((l31 >> 2) & 3);
     a_rd[kk] = static_cast<uint32_t>(row * kBK + c * 8) * 2u;
   }
-  // B-tile column of register slot ni. With two wave rows, slot order is
-  // rotated by wm so that slots 0 and (SwiGLU) 2 / (plain) 1 are the columns
-  // this wave also covers for the extra 32-row block of a 288-row tile.
+  // B-tile column of register slot ni (SwiGLU: slots [0, NI/2) gate, the rest
+  // the matching up columns)
   auto bcol = [&](int ni) {
-    if constexpr (WM == 2) {
-      if (SWIGLU) {
-        const int sub = (ni & 1) ^ wm;  // which 32-wide half of the wave's 64 gate columns
-        return (ni < 2 ? 0 : 128) + wn * 64 + sub * 32;
-      }
-      const int blk = (ni + 2 * wm) & 3;
-      return wn * 128 + blk * 32;
-    } else {
-      constexpr int half = NI / 2;
-      if (SWIGLU) return ni < half ? wn * (128 / WN) + ni * 32 : 128 + wn * (128 / WN) + (ni - half) * 32;
-      return wn * (256 / WN) + ni * 32;
-    }
+    constexpr int half = NI / 2;
+    if (SWIGLU) return ni < half ? wn * (128 / WN) + ni * 32 : 128 + wn * (128 / WN) + (ni - half) * 32;
+    return wn * (256 / WN) + ni * 32;
   };
   uint32_t b_rd[NI];
   {
@@ -239,10 +226,6 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
     if constexpr (MI > 1) f.a[1] = ds_read16<2048>(ab);
     if constexpr (MI > 2) f.a[2] = ds_read16<4096>(ab);
     if constexpr (MI > 3) f.a[3] = ds_read16<6144>(ab);
-    if constexpr (L::EXTRA) {
-      // rows 256..287: the wave-row offset wm*128 is taken back out
-      f.ax = ds_read16<16384>(ab - static_cast<uint32_t>(wm * 128 * kBK * 2));
-    }
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
       const uint32_t bn = bb + b_rd[ni];
@@ -258,7 +241,6 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
   auto tie_frags = [&](Frags& f) {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) tie(f.a[mi]);
-    if constexpr (L::EXTRA) tie(f.ax);
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
       tie(f.b[ni][0]);
@@ -267,19 +249,15 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
   };
 
   f32x16_t acc[MI][NI];
-  f32x16_t accx[2];
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) accx[0][r] = accx[1][r] = 0.f;
 
-  // MFMAs with flat block index in [LO, HI) (row-major over mi, ni); the extra
-  // block's two MFMAs go with the second part.
-  auto mfmas = [&](const Frags& f, auto lo_c, auto hi_c, auto extra_c) {
+  // MFMAs of one 16-wide K slice with flat block index in [LO, HI) (row-major over mi, ni)
+  auto mfmas = [&](const Frags& f, auto lo_c, auto hi_c) {
     constexpr int LO = decltype(lo_c)::value, HI = decltype(hi_c)::value;
 #pragma unroll
     for (int q = LO; q < HI; ++q) {
@@ -287,17 +265,10 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
       acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], join(f.b[ni][0], f.b[ni][1]), acc[mi][ni],
                                                             0, 0, 0);
     }
-    if constexpr (L::EXTRA && decltype(extra_c)::value) {
-      constexpr int s1 = SWIGLU ? 2 : 1;
-      accx[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.ax, join(f.b[0][0], f.b[0][1]), accx[0], 0, 0, 0);
-      accx[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.ax, join(f.b[s1][0], f.b[s1][1]), accx[1], 0, 0, 0);
-    }
   };
   using Z = std::integral_constant<int, 0>;
   using Half = std::integral_constant<int, L::NMFMA / 2>;
   using All = std::integral_constant<int, L::NMFMA>;
-  using No = std::integral_constant<bool, false>;
-  using Yes = std::integral_constant<bool, true>;
 
   // ---- pipeline -------------------------------------------------------------------------
   // Stage s lands in buffer s % kStages; it is issued three stages ahead. When a
@@ -320,33 +291,11 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
 
   for (int ks = 0; ks < ksteps; ++ks) {
     const int buf = ks % kStages;
-    if constexpr (L::EXTRA) {
-      // 288-row tiles keep one fragment set (the extra block's accumulators
-      // take the registers of the second): read, wait, multiply, per slice.
-      wait_lgkmcnt<0>();
-      tie_frags(f0);
-      __builtin_amdgcn_sched_barrier(0);
-      mfmas(f0, Z{}, All{}, Yes{});
-      __builtin_amdgcn_sched_barrier(0);
-      read_frags(f0, buf, 1);
-      wait_lgkmcnt<0>();  // this wave's reads of stage ks are complete
-      tie_frags(f0);
-      if (ks + 1 < ksteps) {
-        wait_stage(ks + 1);
-        __builtin_amdgcn_s_barrier();
-        if (ks + kStages < ksteps) issue(ks + kStages);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      mfmas(f0, Z{}, All{}, Yes{});
-      __builtin_amdgcn_sched_barrier(0);
-      if (ks + 1 < ksteps) read_frags(f0, (ks + 1) % kStages, 0);
-      continue;
-    }
     read_frags(f1, buf, 1);
     wait_lgkmcnt<L::LDS_READS>();
     tie_frags(f0);
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(f0, Z{}, Half{}, No{});
+    mfmas(f0, Z{}, Half{});
     __builtin_amdgcn_sched_barrier(0);
     wait_lgkmcnt<0>();  // this wave's reads of stage ks are complete
     tie_frags(f1);
@@ -356,12 +305,12 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
       if (ks + kStages < ksteps) issue(ks + kStages);
     }
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(f0, Half{}, All{}, Yes{});
+    mfmas(f0, Half{}, All{});
     __builtin_amdgcn_sched_barrier(0);
     // the next stage's first slice is read while this slice's MFMAs run
     if (ks + 1 < ksteps) read_frags(f0, (ks + 1) % kStages, 0);
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(f1, Z{}, All{}, Yes{});
+    mfmas(f1, Z{}, All{});
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -388,24 +337,6 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
         const float v = SWIGLU ? silu_fast(acc[mi][ni][r]) * acc[mi][ni + NI / 2][r] : acc[mi][ni][r];
         __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(v), rc_src, static_cast<int>(row_off + coff[ni]), 0,
                                               0);
-      }
-    }
-  }
-  if constexpr (L::EXTRA) {
-    const uint32_t cx0 = coff[0];
-    const uint32_t cx1 = SWIGLU ? 0u : coff[1];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = 256 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-      const uint32_t row_off = static_cast<uint32_t>(row) * c_row_bytes;
-      if (SWIGLU) {
-        const float v = silu_fast(accx[0][r]) * accx[1][r];
-        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(v), rc_src, static_cast<int>(row_off + cx0), 0, 0);
-      } else {
-        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(accx[0][r]), rc_src, static_cast<int>(row_off + cx0),
-                                              0, 0);
-        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(accx[1][r]), rc_src, static_cast<int>(row_off + cx1),
-                                              0, 0);
       }
     }
   }
