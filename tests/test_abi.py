@@ -112,8 +112,8 @@ def test_workspace_sizes():
     s = _shape(T=0)
     assert lib.moe_dispatch_workspace_bytes(ctypes.byref(s)) == 0
     s = _shape(T=16384, k=8, E=256)
-    # two int32 per (expert, chunk of 1024 pairs): the histogram and the chunk bases
-    assert lib.moe_dispatch_workspace_bytes(ctypes.byref(s)) == 2 * 256 * 128 * 4
+    # per (expert, chunk of 1024 pairs): the histogram and the chunk bases; plus E totals
+    assert lib.moe_dispatch_workspace_bytes(ctypes.byref(s)) == (2 * 256 * 128 + 256) * 4
     assert lib.moe_grouped_gemm_workspace_bytes(ctypes.byref(s), moe.MOE_BF16) == 0
 
 

@@ -7,12 +7,12 @@
 // tamanhos se combinam" (a rank owns one contiguous block of experts, so its
 // pairs are one contiguous segment of the expert-sorted pair list).
 //
-// Design (four small launches, all bounded by the pair count or HBM):
+// Design (five small launches, all bounded by the pair count or HBM):
 //   1. count   : one workgroup per chunk of kDispatchChunk flat pairs builds an
 //                LDS histogram and stores it expert-major: ws[e * n_chunks + c].
-//   2. scan    : one workgroup, one wave per expert, scans the histogram in
-//                expert-major order: counts, offsets, and the first sorted slot
-//                of chunk c's pairs of expert e, stored chunk-major.
+//   2. scan    : two launches with one wave per expert: per-expert totals,
+//                then counts, offsets and the first sorted slot of chunk c's
+//                pairs of expert e, stored chunk-major.
 //   3. scatter : each chunk stages its E first slots in LDS and walks its
 //                pairs in order, 256 at a time. A wave
 //                finds the lanes holding the same expert with a ballot loop;
@@ -47,33 +47,47 @@ __global__ __launch_bounds__(kThreads) void dispatch_count_kernel(const int32_t*
     ws[static_cast<int64_t>(e) * n_chunks + blockIdx.x] = hist[e];
 }
 
-constexpr int kScanThreads = 1024;
-constexpr int kScanWaves = kScanThreads / kWave;
+constexpr int kScanWavesPerBlock = kThreads / kWave;
 
-// Exclusive scan of the (expert, chunk) histogram in expert-major order, one
-// wave per expert: the expert's per-chunk counts are contiguous, read and
-// prefix-summed 64 at a time. Writes counts and offsets, and the first sorted
-// slot of every (chunk, expert) pair chunk-major, base[c * E + e], so that a
-// scatter workgroup reads its E bases as one contiguous row.
-__global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(const int32_t* __restrict__ ws,
-                                                                     int32_t* __restrict__ base,
-                                                                     int32_t* __restrict__ counts,
-                                                                     int32_t* __restrict__ offsets,
-                                                                     int E, int n_chunks) {
-  __shared__ int tot[kMaxExperts + 1];
+// Scan of the (expert, chunk) histogram, in two launches with one wave per
+// expert so that every expert's row is read with many loads in flight:
+//   totals: tot[e] = sum over chunks of the histogram row of expert e;
+//   bases : every workgroup scans the <= 1024 totals in LDS (offsets), then each
+//           wave prefix-sums its expert's row and stores the first sorted slot
+//           of every (chunk, expert) pair chunk-major, base[c * E + e], so that
+//           a scatter workgroup reads its E bases as one contiguous row.
+//           Workgroup 0 also writes counts and offsets.
+__global__ __launch_bounds__(kThreads) void dispatch_zero_counts_kernel(int32_t* __restrict__ counts,
+                                                                        int32_t* __restrict__ offsets, int E) {
+  for (int e = threadIdx.x; e <= E; e += kThreads) {
+    if (e < E) counts[e] = 0;
+    offsets[e] = 0;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void dispatch_totals_kernel(const int32_t* __restrict__ ws,
+                                                                   int32_t* __restrict__ tot, int E,
+                                                                   int n_chunks) {
+  const int lane = lane_id();
+  const int e = blockIdx.x * kScanWavesPerBlock + threadIdx.x / kWave;
+  if (e >= E) return;
+  const int32_t* row = ws + static_cast<int64_t>(e) * n_chunks;
+  int s = 0;
+  for (int c = lane; c < n_chunks; c += kWave) s += row[c];
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  if (lane == 0) tot[e] = s;
+}
+
+__global__ __launch_bounds__(kThreads) void dispatch_bases_kernel(const int32_t* __restrict__ ws,
+                                                                  const int32_t* __restrict__ tot,
+                                                                  int32_t* __restrict__ base,
+                                                                  int32_t* __restrict__ counts,
+                                                                  int32_t* __restrict__ offsets, int E,
+                                                                  int n_chunks) {
+  __shared__ int off_s[kMaxExperts + 1];
   const int lane = lane_id();
   const int wv = threadIdx.x / kWave;
-  // 1. per-expert totals
-  for (int e = wv; e < E; e += kScanWaves) {
-    const int32_t* row = ws + static_cast<int64_t>(e) * n_chunks;
-    int s = 0;
-    for (int c = lane; c < n_chunks; c += kWave) s += row[c];
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
-    if (lane == 0) tot[e] = s;
-  }
-  __syncthreads();
-  // 2. exclusive scan of the totals (E <= 1024) by wave 0, 64 at a time
   if (wv == 0) {
     int carry = 0;
     for (int e0 = 0; e0 < E; e0 += kWave) {
@@ -86,31 +100,35 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(const int32
         if (lane >= off) incl += o;
       }
       if (e < E) {
-        offsets[e] = carry + incl - v;
-        counts[e] = v;
-        tot[e] = carry + incl - v;
+        off_s[e] = carry + incl - v;
+        if (blockIdx.x == 0) {
+          offsets[e] = carry + incl - v;
+          counts[e] = v;
+        }
       }
       carry += __shfl(incl, kWave - 1);
     }
-    if (lane == 0) offsets[E] = carry;
+    if (lane == 0) {
+      off_s[E] = carry;
+      if (blockIdx.x == 0) offsets[E] = carry;
+    }
   }
   __syncthreads();
-  // 3. per-(chunk, expert) bases
-  for (int e = wv; e < E; e += kScanWaves) {
-    const int32_t* row = ws + static_cast<int64_t>(e) * n_chunks;
-    int carry = tot[e];
-    for (int c0 = 0; c0 < n_chunks; c0 += kWave) {
-      const int c = c0 + lane;
-      const int v = c < n_chunks ? row[c] : 0;
-      int incl = v;
+  const int e = blockIdx.x * kScanWavesPerBlock + wv;
+  if (e >= E) return;
+  const int32_t* row = ws + static_cast<int64_t>(e) * n_chunks;
+  int carry = off_s[e];
+  for (int c0 = 0; c0 < n_chunks; c0 += kWave) {
+    const int c = c0 + lane;
+    const int v = c < n_chunks ? row[c] : 0;
+    int incl = v;
 #pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const int o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-      }
-      if (c < n_chunks) base[static_cast<int64_t>(c) * E + e] = carry + incl - v;
-      carry += __shfl(incl, kWave - 1);
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
     }
+    if (c < n_chunks) base[static_cast<int64_t>(c) * E + e] = carry + incl - v;
+    carry += __shfl(incl, kWave - 1);
   }
 }
 
@@ -205,8 +223,9 @@ __global__ __launch_bounds__(kThreads) void dispatch_gather_kernel(
 size_t dispatch_workspace_bytes(int64_t T, int k, int E) {
   const int64_t P = T * k;
   const int64_t n_chunks = (P + kDispatchChunk - 1) / kDispatchChunk;
-  // per-(expert, chunk) counts, then per-(chunk, expert) first slots
-  return 2 * static_cast<size_t>(n_chunks * E) * sizeof(int32_t);
+  if (n_chunks == 0) return 0;
+  // per-(expert, chunk) counts, per-(chunk, expert) first slots, per-expert totals
+  return (2 * static_cast<size_t>(n_chunks * E) + E) * sizeof(int32_t);
 }
 
 hipError_t launch_dispatch(const void* x, size_t row_bytes, const int32_t* idx, int32_t* counts,
@@ -221,9 +240,16 @@ hipError_t launch_dispatch(const void* x, size_t row_bytes, const int32_t* idx, 
                        E, n_chunks);
   }
   int32_t* bases = ws + static_cast<int64_t>(n_chunks) * E;
-  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, ws, bases, counts,
+  int32_t* tot = bases + static_cast<int64_t>(n_chunks) * E;
+  const int scan_blocks = (E + kScanWavesPerBlock - 1) / kScanWavesPerBlock;
+  if (n_chunks == 0) {
+    // no pairs: counts and offsets are all zero (tot is the E zeros the totals pass would give)
+    hipLaunchKernelGGL(dispatch_zero_counts_kernel, dim3(1), dim3(kThreads), 0, stream, counts, offsets, E);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(dispatch_totals_kernel, dim3(scan_blocks), dim3(kThreads), 0, stream, ws, tot, E, n_chunks);
+  hipLaunchKernelGGL(dispatch_bases_kernel, dim3(scan_blocks), dim3(kThreads), 0, stream, ws, tot, bases, counts,
                      offsets, E, n_chunks);
-  if (n_chunks == 0) return hipGetLastError();
   hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(n_chunks), dim3(kThreads), 0, stream, idx, bases,
                      offsets, perm, pair_pos, P, E, e_begin, e_end);
   const int row_vec = static_cast<int>(row_bytes / 16);

@@ -9,8 +9,9 @@
 // VPL logits in registers, expert e = g + v*G, so a group's loads are contiguous.
 // A logit and its id form one 64-bit key (order-preserving float bits << 32 |
 // ~id), so "larger value, then lower id" is a plain unsigned max and every key
-// is unique. Each of the k rounds is a register max plus a log2(G)-step
-// butterfly; the owning lane then retires its key. HBM-bound: T*E*4 bytes read.
+// is unique. Each of the k rounds is a register max plus a group maximum
+// (DPP moves inside each 16-lane row, readlane across rows); the owning lane
+// then retires its key. HBM-bound: T*E*4 bytes read.
 #include "moe_internal.h"
 
 namespace moe {
@@ -27,10 +28,43 @@ __device__ __forceinline__ float from_orderable(uint32_t o) {
   return __uint_as_float(u);
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
-  const int lo = __shfl_xor(static_cast<int>(static_cast<uint32_t>(v)), mask);
-  const int hi = __shfl_xor(static_cast<int>(static_cast<uint32_t>(v >> 32)), mask);
+// 64-bit DPP move within a row of 16 lanes (every lane reads a lane of its own row).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v)), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v >> 32)), CTRL, 0xF, 0xF,
+                                             false);
   return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), lane);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), lane);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+constexpr int kQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+// Maximum over each aligned group of G lanes, returned to every lane of the
+// group: DPP steps inside a row of 16, then the row maxima by readlane.
+template <int G>
+__device__ __forceinline__ uint64_t group_max(uint64_t v) {
+  if constexpr (G >= 2) v = umax64(v, dpp_u64<kQuadSwap1>(v));
+  if constexpr (G >= 4) v = umax64(v, dpp_u64<kQuadSwap2>(v));
+  if constexpr (G >= 8) v = umax64(v, dpp_u64<kRowHalfMirror>(v));
+  if constexpr (G >= 16) v = umax64(v, dpp_u64<kRowMirror>(v));
+  if constexpr (G >= 32) {
+    const uint64_t r01 = umax64(readlane_u64(v, 0), readlane_u64(v, 16));
+    const uint64_t r23 = umax64(readlane_u64(v, 32), readlane_u64(v, 48));
+    if constexpr (G == 32) v = lane_id() < 32 ? r01 : r23;
+    else v = umax64(r01, r23);
+  }
+  return v;
 }
 
 template <int G, int VPL>
@@ -69,11 +103,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     uint64_t best = key[0];
 #pragma unroll
     for (int v = 1; v < VPL; ++v) best = key[v] > best ? key[v] : best;
-#pragma unroll
-    for (int off = G / 2; off > 0; off >>= 1) {
-      const uint64_t o = shfl_xor_u64(best, off);
-      best = o > best ? o : best;
-    }
+    best = group_max<G>(best);
 #pragma unroll
     for (int v = 0; v < VPL; ++v)
       if (key[v] == best) key[v] = 0;  // keys are unique: only the owner matches
