@@ -11,6 +11,7 @@ fp64 oracle on a bounded sample of the same workload, timed on the host cores.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -28,6 +29,9 @@ METRIC = "routed tokens/sec per MoE layer fwd on 1 MI355X; grouped-GEMM % MFMA p
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0
+# Sources that decide the grouped GEMM's machine code; a stored traffic figure is
+# reported only while they are unchanged since its counters were taken.
+GEMM_SOURCES = ["gemm_common.h", "moe_internal.h", "grouped_gemm.hip", "grouped_gemm_lds.hip"]
 
 
 def host_cores() -> int:
@@ -39,6 +43,32 @@ def host_cores() -> int:
     if omp and omp.isdigit():
         n = min(n, int(omp))
     return n
+
+
+def gemm_sources_sha256() -> str:
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "token_dispatch_grouped_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per step of the grouped GEMM from the FETCH_SIZE / WRITE_SIZE
+    summary under profiles/, or None if there is none for this workload or the
+    kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"grouped_gemm_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if " = " in line:
+                key, val = line.strip().split(" = ", 1)
+                kv[key] = val
+    if kv.get("workload") != workload or kv.get("gemm_sources_sha256") != gemm_sources_sha256():
+        return None
+    return int(kv["traffic_bytes_per_step"])
 
 
 def cpu_baseline(w: mi.Workload, logits, x, wgu, wdn, budget_s: float = 12.0) -> dict:
@@ -147,17 +177,27 @@ def main() -> int:
     gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
     flops = 6.0 * n_loc * w.d * w.d_ff  # gate/up (4 N d d_ff) + down (2 N d d_ff)
-    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
-    achieved = flops / (gemm_ms * 1e-3) / 1e12
+    b = 2 if w.dtype == "bf16" else 4
+    # weights of every active local expert once, x_perm and H read once, H and Y written once
+    gemm_bytes = 3.0 * active * w.d * w.d_ff * b + 2.0 * n_loc * (w.d + w.d_ff) * b
+    peak_flops = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    t_gemm = gemm_ms * 1e-3
+    # the bound is whichever of MFMA time and HBM time is longer at peak
+    if w.dtype == "bf16" and gemm_bytes / (PEAK_HBM_GBS * 1e9) > flops / (peak_flops * 1e12):
+        bound, achieved, peak, unit = "hbm", gemm_bytes / t_gemm / 1e9, PEAK_HBM_GBS, "GB/s"
+    else:
+        bound = "mfma" if w.dtype == "bf16" else "alu"
+        achieved, peak, unit = flops / t_gemm / 1e12, peak_flops, "TFLOP/s"
     roofline = {
         "kernel": "moe_grouped_gemm (gate/up+SwiGLU launch, then down launch)",
-        "bound": "mfma" if w.dtype == "bf16" else "alu",
+        "bound": bound,
         "achieved": round(achieved, 2),
         "peak": peak,
-        "unit": "TFLOP/s",
+        "unit": unit,
         "frac": round(achieved / peak, 4),
-        "traffic": None,
+        "traffic": stored_traffic(w.name),
         "flops_per_launch": flops,
+        "algorithmic_bytes_per_launch": gemm_bytes,
         "avg_ms": round(gemm_ms, 4),
     }
     result = {
@@ -176,9 +216,28 @@ def main() -> int:
         "config": {"workload": w.name, "T": w.T, "d": w.d, "d_ff": w.d_ff, "E": w.E, "k": w.k,
                    "local_experts": [w.e_begin, w.e_end], "N_loc": n_loc, "active_local_experts": active,
                    "parallelism": "one rank's share on 1 GPU"},
+        "local_pairs_per_s": round(n_loc / (ms_step * 1e-3), 1),
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    # per entry point, in a separate untimed pass: events between the four calls
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        e = evs[i]
+        e[0].record(stream)
+        moe.route_topk(dl, w.k, idx, wts, stream=stream)
+        e[1].record(stream)
+        moe.dispatch(dx, idx, w.E, w.e_begin, w.e_end, out=disp, stream=stream)
+        e[2].record(stream)
+        moe.grouped_gemm(disp.x_perm, disp.offsets, dgu, ddn, w.T, w.k, w.E, w.e_begin, w.e_end,
+                         h=h, y=y, stream=stream)
+        e[3].record(stream)
+        moe.combine(y, disp.pair_pos, wts, w.T, w.k, w.E, w.e_begin, w.e_end, out=out, stream=stream)
+        e[4].record(stream)
+    torch.cuda.synchronize()
+    parts = ["route_topk", "dispatch", "grouped_gemm", "combine"]
+    result["entry_point_ms"] = {p: round(float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])), 4)
+                                for j, p in enumerate(parts)}
     del dgu, ddn
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, logits, x, wgu, wdn)

@@ -150,7 +150,8 @@ moe_status moe_grouped_gemm(const moe_shape* s, moe_dtype dt, const void* x_perm
  * accumulated in fp32 in slot order, rounded once to dt. A token with no local
  * pair gets a zero row; every one of the T rows is written.
  *   y        [N_max, d] dt, read only.
- *   pair_pos [T*k] int32, read only (values must be -1 or < N_max).
+ *   pair_pos [T*k] int32, read only: a local row in [0, N_max), or -1; any other
+ *            value (negative or >= N_max) is treated as -1 and contributes nothing.
  *   topk_w   [T, k] fp32, read only.
  *   out      [T, d] dt, written. */
 moe_status moe_combine(const moe_shape* s, moe_dtype dt, const void* y,
