@@ -83,6 +83,14 @@ __device__ __forceinline__ void wait_lgkmcnt() {
   else static_assert(N == 0, "add the count");
 }
 
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ void tie(T& v) {
   asm volatile("" : "+v"(v));
@@ -178,18 +186,7 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
     b_voff[jj] = (static_cast<uint32_t>(kl) * static_cast<uint32_t>(ldb) + static_cast<uint32_t>(col)) * 2u;
   }
 
-  auto issue = [&](int s) {
-    const int buf = s % kStages;
-    const __amdgpu_buffer_rsrc_t ra =
-        make_rsrc(a_tile + s * kBK, a_bytes - static_cast<uint32_t>(s) * kBK * 2u);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bexp + static_cast<int64_t>(s) * kBK * ldb,
-                                                b_bytes - static_cast<uint32_t>(s) * kBK * ldb * 2u);
-#pragma unroll
-    for (int jj = 0; jj < L::A_PER_WAVE; ++jj)
-      dma16(ra, a_voff[jj], sA_base + buf * kAStageBytes + a_slot[jj] * 1024);
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) dma16(rb, b_voff[jj], sB_base + buf * kBStageBytes + (wave * 4 + jj) * 1024);
-  };
+
 
   // ---- fragment reads ----------------------------------------------------------------
   const int l31 = lane & 31;
@@ -218,24 +215,17 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
     }
   }
   const uint32_t sA_addr = sA_base, sB_addr = sB_base;
+  constexpr int R = L::LDS_READS, NM = L::NMFMA;
 
-  auto read_frags = [&](Frags& f, int buf, int kk) {
-    const uint32_t ab = sA_addr + buf * kAStageBytes + a_rd[kk];
-    const uint32_t bb = sB_addr + buf * kBStageBytes;
-    if constexpr (MI > 0) f.a[0] = ds_read16<0>(ab);
-    if constexpr (MI > 1) f.a[1] = ds_read16<2048>(ab);
-    if constexpr (MI > 2) f.a[2] = ds_read16<4096>(ab);
-    if constexpr (MI > 3) f.a[3] = ds_read16<6144>(ab);
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni) {
-      const uint32_t bn = bb + b_rd[ni];
-      if (kk == 0) {
-        f.b[ni][0] = ds_read_tr<0>(bn);
-        f.b[ni][1] = ds_read_tr<2048>(bn);
-      } else {
-        f.b[ni][0] = ds_read_tr<8192>(bn);
-        f.b[ni][1] = ds_read_tr<10240>(bn);
-      }
+  // LDS read number r of a 16-wide K slice kk: r < MI an activation block, then
+  // the two 4-k halves of each weight block.
+  auto read_one = [&](Frags& f, int buf, auto kk_c, auto r_c) {
+    constexpr int kk = decltype(kk_c)::value, r = decltype(r_c)::value;
+    if constexpr (r < MI) {
+      f.a[r] = ds_read16<r * 2048>(sA_addr + buf * kAStageBytes + a_rd[kk]);
+    } else {
+      constexpr int ni = (r - MI) / 2, h = (r - MI) % 2;
+      f.b[ni][h] = ds_read_tr<kk * 8192 + h * 2048>(sB_addr + buf * kBStageBytes + b_rd[ni]);
     }
   };
   auto tie_frags = [&](Frags& f) {
@@ -256,19 +246,31 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
-  // MFMAs of one 16-wide K slice with flat block index in [LO, HI) (row-major over mi, ni)
-  auto mfmas = [&](const Frags& f, auto lo_c, auto hi_c) {
-    constexpr int LO = decltype(lo_c)::value, HI = decltype(hi_c)::value;
-#pragma unroll
-    for (int q = LO; q < HI; ++q) {
-      const int mi = q / NI, ni = q % NI;
-      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], join(f.b[ni][0], f.b[ni][1]), acc[mi][ni],
-                                                            0, 0, 0);
-    }
+  // MFMA number q of a slice (row-major over mi, ni)
+  auto mfma_one = [&](const Frags& f, auto q_c) {
+    constexpr int q = decltype(q_c)::value, mi = q / NI, ni = q % NI;
+    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], join(f.b[ni][0], f.b[ni][1]), acc[mi][ni], 0, 0,
+                                                          0);
   };
-  using Z = std::integral_constant<int, 0>;
-  using Half = std::integral_constant<int, L::NMFMA / 2>;
-  using All = std::integral_constant<int, L::NMFMA>;
+
+  // ---- DMA, one instruction at a time -------------------------------------------------
+  struct StageLoads {
+    __amdgpu_buffer_rsrc_t ra, rb;
+    uint32_t la, lb;  // LDS byte addresses of the stage's buffers
+  };
+  auto stage_loads = [&](int s) {
+    const int buf = s % kStages;
+    return StageLoads{make_rsrc(a_tile + s * kBK, a_bytes - static_cast<uint32_t>(s) * kBK * 2u),
+                      make_rsrc(Bexp + static_cast<int64_t>(s) * kBK * ldb,
+                                b_bytes - static_cast<uint32_t>(s) * kBK * ldb * 2u),
+                      sA_base + buf * kAStageBytes, sB_base + buf * kBStageBytes};
+  };
+  // load j of a stage: j < A_PER_WAVE activations, then this wave's 4 weight loads
+  auto dma_one = [&](const StageLoads& st, auto j_c) {
+    constexpr int j = decltype(j_c)::value;
+    if constexpr (j < L::A_PER_WAVE) dma16(st.ra, a_voff[j], st.la + a_slot[j] * 1024);
+    else dma16(st.rb, b_voff[j - L::A_PER_WAVE], st.lb + (wave * 4 + (j - L::A_PER_WAVE)) * 1024);
+  };
 
   // ---- pipeline -------------------------------------------------------------------------
   // Stage s lands in buffer s % kStages; it is issued three stages ahead. When a
@@ -280,39 +282,70 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
     else if (after == 1) wait_vmcnt<PER>();
     else wait_vmcnt<0>();
   };
-#pragma unroll
-  for (int s = 0; s < kStages - 1; ++s)
-    if (s < ksteps) issue(s);
-  wait_stage(0);
-  __builtin_amdgcn_s_barrier();
-  if (kStages - 1 < ksteps) issue(kStages - 1);
-  Frags f0, f1;
-  read_frags(f0, 0, 0);
+  using K0 = std::integral_constant<int, 0>;
+  using K1 = std::integral_constant<int, 1>;
 
-  for (int ks = 0; ks < ksteps; ++ks) {
+  // One stage. With a single wave per SIMD, the matrix unit idles whenever the
+  // wave stops to issue a burst of other instructions, so every LDS read and
+  // every DMA load is issued in the shadow of an MFMA: slice 0 (fragments f0)
+  // carries slice 1's reads, one per MFMA; then the stage barrier; slice 1
+  // carries the next stage's slice-0 reads, one per MFMA, and the DMA of stage
+  // ks + kStages, one per two MFMAs.
+  Frags f0, f1;
+  auto stage = [&](int ks, auto dma_c, auto more_c) {
+    constexpr bool DMA = decltype(dma_c)::value, MORE = decltype(more_c)::value;
     const int buf = ks % kStages;
-    read_frags(f1, buf, 1);
-    wait_lgkmcnt<L::LDS_READS>();
+    wait_lgkmcnt<0>();  // f0 (read during the previous stage) has landed
     tie_frags(f0);
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(f0, Z{}, Half{});
-    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, NM>([&](auto q) {
+      mfma_one(f0, q);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (decltype(q)::value < R) read_one(f1, buf, K1{}, q);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    static_for<(NM < R ? NM : R), R>([&](auto r) { read_one(f1, buf, K1{}, r); });
     wait_lgkmcnt<0>();  // this wave's reads of stage ks are complete
     tie_frags(f1);
-    if (ks + 1 < ksteps) {
+    if constexpr (MORE) {
       wait_stage(ks + 1);
       __builtin_amdgcn_s_barrier();  // stage ks+1 landed for every wave; nobody reads stage ks any more
-      if (ks + kStages < ksteps) issue(ks + kStages);
     }
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(f0, Half{}, All{});
+    StageLoads st;
+    if constexpr (DMA) st = stage_loads(ks + kStages);
+    const int nbuf = (ks + 1) % kStages;
+    static_for<0, NM>([&](auto q_c) {
+      constexpr int q = decltype(q_c)::value;
+      mfma_one(f1, q_c);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (MORE && q < R) read_one(f0, nbuf, K0{}, q_c);
+      if constexpr (DMA && q % 2 == 0 && q / 2 < PER) dma_one(st, std::integral_constant<int, q / 2>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if constexpr (MORE) static_for<(NM < R ? NM : R), R>([&](auto r) { read_one(f0, nbuf, K0{}, r); });
+    if constexpr (DMA) static_for<((NM + 1) / 2 < PER ? (NM + 1) / 2 : PER), PER>([&](auto j) { dma_one(st, j); });
     __builtin_amdgcn_sched_barrier(0);
-    // the next stage's first slice is read while this slice's MFMAs run
-    if (ks + 1 < ksteps) read_frags(f0, (ks + 1) % kStages, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(f1, Z{}, All{});
-    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // prologue: stages 0..kStages-2 in flight, stage 0 landed, stage kStages-1
+  // issued, slice 0 of stage 0 requested
+  for (int s = 0; s < kStages - 1 && s < ksteps; ++s) {
+    const StageLoads st = stage_loads(s);
+    static_for<0, PER>([&](auto j) { dma_one(st, j); });
   }
+  wait_stage(0);
+  __builtin_amdgcn_s_barrier();
+  if (kStages - 1 < ksteps) {
+    const StageLoads st = stage_loads(kStages - 1);
+    static_for<0, PER>([&](auto j) { dma_one(st, j); });
+  }
+  static_for<0, R>([&](auto r) { read_one(f0, 0, K0{}, r); });
+
+  int ks = 0;
+  for (; ks + kStages < ksteps; ++ks) stage(ks, std::true_type{}, std::true_type{});
+  for (; ks + 1 < ksteps; ++ks) stage(ks, std::false_type{}, std::true_type{});
+  stage(ks, std::false_type{}, std::false_type{});
 
   // ---- epilogue: bf16 results through buffer stores over the tile's valid rows --------
   const __amdgpu_buffer_rsrc_t rc_src = make_rsrc(
