@@ -10,8 +10,8 @@
 // projection.
 //
 // Design (gfx950):
-//   * Four LDS stages of K = 32 (16 KB of activations + 16 KB of weights each,
-//     128 KB in all). Each stage is filled by buffer_load ... lds (16 bytes per
+//   * Four LDS stages of K = 32 (18 KB of activations, room for 288 rows, + 16 KB
+//     of weights each, 136 KB in all). Each stage is filled by buffer_load ... lds (16 bytes per
 //     lane, written to LDS without passing through registers), issued three
 //     stages ahead of its use, so about 3 x 1000 MFMA cycles of HBM/L2 latency
 //     are covered without staging registers.
@@ -22,13 +22,18 @@
 //     each 4 (k) x 16 (n) block into per-lane 4-k columns, two of which form a
 //     v_mfma_f32_32x32x16_bf16 B operand. No weight repacking, no VALU transpose.
 //   * LDS reads are issued by inline asm with explicit lgkmcnt waits, so the
-//     compiler does not serialise them behind the outstanding LDS-DMA loads;
-//     fragments for the next 16-wide K slice are read while the current slice's
-//     16 MFMAs run, and sched_barriers keep that interleave in place.
-//   * Row tiles are 256 rows, except an expert's last tile, which takes the
-//     smallest of 32/64/128/256 rows that covers it, so a ragged tail costs a
-//     fraction of a full tile. Wave layouts: 2 x 2 waves of (H/2) x 128 for
-//     H >= 64, 1 x 4 waves of 32 x 64 for H = 32.
+//     compiler does not serialise them behind the outstanding LDS-DMA loads.
+//     Fragments for the next 16-wide K slice are read while the current slice's
+//     MFMAs run, one read after each MFMA, and the DMA loads go one after every
+//     second MFMA: with one wave per SIMD, a burst of other instructions would
+//     leave the matrix unit idle. sched_barriers keep that order in place.
+//   * Row tiles are 256 rows. A remainder of at most 32 rows rides on the
+//     expert's last full tile, which becomes 288 rows: every wave also takes
+//     half of its weight blocks against the shared 32-row block (their two
+//     accumulators live in VGPRs, the other 256 registers being full). A larger
+//     remainder gets its own tile of the smallest of 32/64/128/256 rows that
+//     covers it. Wave layouts: 2 x 2 waves of (H/2) x 128 for H >= 64, 1 x 4
+//     waves of 32 x 64 for H = 32.
 //   * Tile walk, XCD mapping and the buffer-store epilogue follow the
 //     register-staged kernel.
 #include <type_traits>
@@ -47,8 +52,8 @@ typedef short i16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kBK = 32;                       // K per stage
 constexpr int kStages = 4;
-constexpr int kARows = 256;                   // rows an activation stage holds
-constexpr int kAStageElems = kARows * kBK;    // 16 KB
+constexpr int kARows = 288;                   // rows an activation stage holds
+constexpr int kAStageElems = kARows * kBK;    // 18 KB
 constexpr int kBStageElems = 256 * kBK;       // 16 KB
 constexpr uint32_t kAStageBytes = kAStageElems * 2;
 constexpr uint32_t kBStageBytes = kBStageElems * 2;
@@ -116,27 +121,37 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS3 void*)(uintptr_t)lds_base, 16, voff, 0, 0, 0);
 }
 
+// c += a * b with c held in VGPRs
+__device__ __forceinline__ void mfma_in_vgprs(f32x16_t& c, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+
 __device__ __forceinline__ bf16x8_t join(i16x4_t lo, i16x4_t hi) {
   return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 struct Frags {
-  bf16x8_t a[4];   // A blocks (32 rows each)
+  bf16x8_t a[5];   // A blocks (32 rows each); a[MI] is the extra block of a 288-row tile
   i16x4_t b[4][2]; // B blocks (32 columns each), two 4-k halves
 };
 
-// H = rows of the tile: 32, 64, 128 or 256.
+// H = rows of the tile: 32, 64, 128, 256 or 288. A 288-row tile is a 256-row
+// tile plus one 32-row block (rows 256..287) that every wave shares: each wave
+// computes it against half of its own weight blocks.
 template <int H>
 struct Layout {
   static constexpr int WM = H >= 64 ? 2 : 1;       // waves along M
   static constexpr int WN = 4 / WM;                // waves along N
-  static constexpr int MI = H / WM / 32;           // 32-row MFMA blocks per wave
+  static constexpr int MI = H / WM / 32;           // 32-row MFMA blocks per wave (regular part)
   static constexpr int NI = 256 / WN / 32;         // 32-column MFMA blocks per wave
+  static constexpr int XR = (H - WM * MI * 32) / 32;  // shared extra row blocks (0 or 1)
+  static constexpr int MX = XR ? NI / 2 : 0;       // extra MFMA blocks per wave
   static constexpr int A_INSTR = H / 16;           // 1 KB DMA instructions per activation stage
   static constexpr int A_PER_WAVE = (A_INSTR + 3) / 4;
   static constexpr int PER = 4 + A_PER_WAVE;       // DMA instructions per stage per wave
-  static constexpr int LDS_READS = MI + 2 * NI;
-  static constexpr int NMFMA = MI * NI;            // regular MFMAs per 16-wide K slice
+  static constexpr int LDS_READS = MI + XR + 2 * NI;
+  static constexpr int NMFMA = MI * NI + MX;       // MFMAs per 16-wide K slice
+  static_assert(XR == 0 || (XR == 1 && WM == 2), "one shared extra row block, two waves along M");
 };
 
 template <bool SWIGLU, int H>
@@ -190,17 +205,23 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
 
   // ---- fragment reads ----------------------------------------------------------------
   const int l31 = lane & 31;
-  uint32_t a_rd[2];
+  uint32_t a_rd[2], a_rd_x[2];
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     const int row = wm * (MI * 32) + l31;
     const int c = (2 * kk + (lane >> 5)) ^ ((l31 >> 2) & 3);
     a_rd[kk] = static_cast<uint32_t>(row * kBK + c * 8) * 2u;
+    a_rd_x[kk] = static_cast<uint32_t>((WM * MI * 32 + l31) * kBK + c * 8) * 2u;  // extra row block
   }
   // B-tile column of register slot ni (SwiGLU: slots [0, NI/2) gate, the rest
-  // the matching up columns)
+  // the matching up columns). In a 288-row tile the second wave row holds its
+  // blocks in swapped slots, so that every wave's share of the extra row block
+  // uses slots 0 and X1 = (SwiGLU ? NI/2 : 1): the gate/up pair, or two plain
+  // blocks, that the other wave row does not take.
+  constexpr int X1 = SWIGLU ? NI / 2 : 1;
   auto bcol = [&](int ni) {
     constexpr int half = NI / 2;
+    if (L::XR) ni = wm ? (SWIGLU ? ni ^ 1 : ni ^ 2) : ni;
     if (SWIGLU) return ni < half ? wn * (128 / WN) + ni * 32 : 128 + wn * (128 / WN) + (ni - half) * 32;
     return wn * (256 / WN) + ni * 32;
   };
@@ -223,14 +244,16 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
     constexpr int kk = decltype(kk_c)::value, r = decltype(r_c)::value;
     if constexpr (r < MI) {
       f.a[r] = ds_read16<r * 2048>(sA_addr + buf * kAStageBytes + a_rd[kk]);
+    } else if constexpr (r < MI + L::XR) {
+      f.a[MI] = ds_read16<0>(sA_addr + buf * kAStageBytes + a_rd_x[kk]);
     } else {
-      constexpr int ni = (r - MI) / 2, h = (r - MI) % 2;
+      constexpr int ni = (r - MI - L::XR) / 2, h = (r - MI - L::XR) % 2;
       f.b[ni][h] = ds_read_tr<kk * 8192 + h * 2048>(sB_addr + buf * kBStageBytes + b_rd[ni]);
     }
   };
   auto tie_frags = [&](Frags& f) {
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) tie(f.a[mi]);
+    for (int mi = 0; mi < MI + L::XR; ++mi) tie(f.a[mi]);
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
       tie(f.b[ni][0]);
@@ -245,12 +268,27 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
     for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+  f32x16_t acc_x[L::MX > 0 ? L::MX : 1];  // this wave's share of the extra row block
+#pragma unroll
+  for (int x = 0; x < L::MX; ++x)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc_x[x][r] = 0.f;
 
-  // MFMA number q of a slice (row-major over mi, ni)
+  // MFMA number q of a slice: first this wave's share of the extra row block (so
+  // that its results, written outside the compiler's view, are next read at least
+  // NMFMA - MX MFMAs later, also in the last slice), then row-major over mi, ni.
   auto mfma_one = [&](const Frags& f, auto q_c) {
-    constexpr int q = decltype(q_c)::value, mi = q / NI, ni = q % NI;
-    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], join(f.b[ni][0], f.b[ni][1]), acc[mi][ni], 0, 0,
-                                                          0);
+    constexpr int q = decltype(q_c)::value;
+    if constexpr (q < L::MX) {
+      // The accumulators are full; these two live in ordinary VGPRs, which the
+      // compiler only allocates for an MFMA written out here.
+      constexpr int ni = q == 0 ? 0 : X1;
+      mfma_in_vgprs(acc_x[q], f.a[MI], join(f.b[ni][0], f.b[ni][1]));
+    } else {
+      constexpr int mi = (q - L::MX) / NI, ni = (q - L::MX) % NI;
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], join(f.b[ni][0], f.b[ni][1]), acc[mi][ni], 0,
+                                                            0, 0);
+    }
   };
 
   // ---- DMA, one instruction at a time -------------------------------------------------
@@ -373,6 +411,22 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
       }
     }
   }
+  if constexpr (L::MX > 0) {  // the extra row block: slot 0 (with its up pair X1 for SwiGLU), or slots 0 and 1
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = WM * MI * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+      const uint32_t row_off = static_cast<uint32_t>(row) * c_row_bytes;
+      if constexpr (SWIGLU) {
+        const float v = silu_fast(acc_x[0][r]) * acc_x[1][r];
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(v), rc_src, static_cast<int>(row_off + coff[0]), 0, 0);
+      } else {
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(acc_x[x][r]), rc_src,
+                                                static_cast<int>(row_off + coff[x]), 0, 0);
+      }
+    }
+  }
 }
 
 template <bool SWIGLU>
@@ -381,7 +435,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_lds_kernel(
     const int32_t* __restrict__ offsets, int e_begin, int e_loc, int K, int N, int ldb, int n_max) {
   __shared__ __attribute__((aligned(1024))) uint16_t smem[kStages * (kAStageElems + kBStageElems)];
   __shared__ TileMap tm;
-  build_tile_map<256>(tm, offsets, e_begin, e_loc, n_max);
+  // a remainder of at most 32 rows rides on the expert's last full tile (288 rows)
+  build_tile_map<256, 32>(tm, offsets, e_begin, e_loc, n_max);
 
   constexpr int kOutCols = SWIGLU ? 128 : 256;
   const int n_tiles = (N + kOutCols - 1) / kOutCols;
@@ -396,7 +451,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_lds_kernel(
     const int rows_valid = tc.mt == mt_e - 1 ? row_end - row0 : 256;
     const int n0 = tc.nt * kOutCols;
     const uint16_t* Bexp = B + static_cast<int64_t>(tc.e) * b_expert;
-    if (rows_valid > 128)
+    if (rows_valid > 256)
+      gemm_tile<SWIGLU, 288>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb);
+    else if (rows_valid > 128)
       gemm_tile<SWIGLU, 256>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb);
     else if (rows_valid > 64)
       gemm_tile<SWIGLU, 128>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb);
