@@ -71,6 +71,41 @@ def stored_traffic(workload: str):
     return int(kv["traffic_bytes_per_step"])
 
 
+def sample_sclk(step, seconds: float, torch):
+    """Median shader clock (MHz) reported by rocm-smi while `step` runs back to back."""
+    import re
+    import subprocess
+    import threading
+
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                out = subprocess.run(["rocm-smi", "--showclocks", "--csv"], capture_output=True,
+                                     text=True, timeout=10).stdout
+            except (OSError, subprocess.SubprocessError):
+                return
+            lines = [l for l in out.splitlines() if l.startswith("card0")]
+            if lines:
+                mhz = re.findall(r"\((\d+)Mhz\)", lines[0])
+                if len(mhz) >= 2:
+                    samples.append(int(mhz[1]))  # fields: mclk, then sclk
+            stop.wait(0.3)
+
+    th = threading.Thread(target=sampler)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    samples = samples[2:] or samples  # the first samples may precede the clock settling
+    return float(np.median(samples)) if samples else None
+
+
 def cpu_baseline(w: mi.Workload, logits, x, wgu, wdn, budget_s: float = 12.0) -> dict:
     """The oracle, as it stands, on the first T_s tokens of the same workload."""
     import oracle
@@ -98,6 +133,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dense8", choices=sorted(mi.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--clock-seconds", type=float, default=0.0,
+                    help="after timing, repeat the step for this many seconds while sampling the "
+                         "shader clock with rocm-smi; reports the median as sclk_mhz")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (3 times), the "
                          "reference for scaling FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -238,6 +276,8 @@ def main() -> int:
     parts = ["route_topk", "dispatch", "grouped_gemm", "combine"]
     result["entry_point_ms"] = {p: round(float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])), 4)
                                 for j, p in enumerate(parts)}
+    if args.clock_seconds > 0:
+        result["sclk_mhz"] = sample_sclk(step, args.clock_seconds, torch)
     del dgu, ddn
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, logits, x, wgu, wdn)
