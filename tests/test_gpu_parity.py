@@ -61,7 +61,8 @@ def _layer_case(w: mi.Workload, logits=None):
 # ----------------------------------------------------------------------------- route top-k
 
 @pytest.mark.parametrize("T,E,k", [(1, 1, 1), (7, 2, 2), (33, 3, 2), (257, 8, 2), (129, 8, 8), (100, 100, 7),
-                                   (300, 128, 4), (65, 256, 8), (10, 1024, 3), (3, 1024, 1024), (0, 16, 4)])
+                                   (300, 128, 4), (65, 256, 8), (10, 1024, 3), (3, 1024, 1024), (0, 16, 4),
+                                   (77, 512, 16), (50, 64, 6), (90, 1000, 33), (40, 12, 5)])
 def test_route_topk_matches_oracle(T, E, k):
     rng = np.random.default_rng(T * 1000 + E * 10 + k)
     logits = rng.standard_normal((T, E)).astype(np.float32)
@@ -71,7 +72,7 @@ def test_route_topk_matches_oracle(T, E, k):
     np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=0, atol=g.W_ATOL)
 
 
-@pytest.mark.parametrize("E,k", [(8, 2), (128, 4), (256, 8), (40, 40)])
+@pytest.mark.parametrize("E,k", [(8, 2), (128, 4), (256, 8), (40, 40), (512, 16), (1024, 9)])
 def test_route_topk_ties_and_signed_zeros(E, k):
     rng = np.random.default_rng(E + k)
     T = 500

@@ -8,9 +8,11 @@
 //
 // Design: one wave per token (grid-stride). The token's k row indices and
 // weights come in with one vector load (a lane per slot); a ballot gives the
-// local slots, visited in slot order through readlane, and a token with none
-// writes its zero row directly. Each lane owns 16-byte column chunks and keeps
-// kChunks of them in flight per slot. HBM-bound: N_loc*d*b read + T*d*b written.
+// local slots, visited in slot order through readlane two at a time (both rows'
+// loads in flight together), and a token with none writes its zero row
+// directly. Each lane owns kChunks 16-byte column chunks per pass; loads and
+// stores go through buffer resources bounded by the row, so there is no branch
+// between them. HBM-bound: N_loc*d*b read + T*d*b written.
 #include "moe_internal.h"
 
 namespace moe {
@@ -83,6 +85,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint4* __restri
       continue;
     }
     for (int c0 = 0; c0 < row_vec; c0 += kChunks * kWave) {
+      // buffers over this block of kChunks * kWave vectors of a row: lanes past the
+      // row end load zero and their stores are dropped, with no branch
+      const uint32_t bytes = static_cast<uint32_t>(min(kChunks * kWave, row_vec - c0)) * 16u;
       float acc[kChunks][V::kN];
 #pragma unroll
       for (int q = 0; q < kChunks; ++q)
@@ -93,32 +98,54 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint4* __restri
         const int rl = j < k ? pair_pos[pbase + j] : -1;
         const float wl = j < k ? w[pbase + j] : 0.f;
         uint64_t mask = __ballot(rl >= 0 && rl < n_max);
+        // local slots two at a time, both rows' loads in flight together, added in slot order
         while (mask) {
-          const int src = __ffsll(static_cast<unsigned long long>(mask)) - 1;
+          const int s0 = __ffsll(static_cast<unsigned long long>(mask)) - 1;
           mask &= mask - 1;
-          const int r = __builtin_amdgcn_readlane(rl, src);
-          const float wj = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wl), src));
-          const uint4* row = y + static_cast<int64_t>(r) * row_vec;
-          uint4 v[kChunks];
-#pragma unroll
-          for (int q = 0; q < kChunks; ++q) {
-            const int c = c0 + q * kWave + lane;
-            v[q] = c < row_vec ? row[c] : make_uint4(0, 0, 0, 0);
+          const int r0 = __builtin_amdgcn_readlane(rl, s0);
+          const float w0 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wl), s0));
+          const bool two = mask != 0;
+          int r1 = 0;
+          float w1 = 0.f;
+          if (two) {
+            const int s1 = __ffsll(static_cast<unsigned long long>(mask)) - 1;
+            mask &= mask - 1;
+            r1 = __builtin_amdgcn_readlane(rl, s1);
+            w1 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wl), s1));
           }
+          const __amdgpu_buffer_rsrc_t b0 = make_rsrc(y + static_cast<int64_t>(r0) * row_vec + c0, bytes);
+          const __amdgpu_buffer_rsrc_t b1 = make_rsrc(y + static_cast<int64_t>(r1) * row_vec + c0, two ? bytes : 0u);
+          uint4 v0[kChunks], v1[kChunks];
+#pragma unroll
+          for (int q = 0; q < kChunks; ++q) v0[q] = buffer_load16(b0, static_cast<uint32_t>(q * kWave + lane) * 16u);
+#pragma unroll
+          for (int q = 0; q < kChunks; ++q) v1[q] = buffer_load16(b1, static_cast<uint32_t>(q * kWave + lane) * 16u);
+          __builtin_amdgcn_sched_barrier(0);  // all eight loads in flight before the first use
 #pragma unroll
           for (int q = 0; q < kChunks; ++q) {
             float f[V::kN];
-            V::load(v[q], f);
+            V::load(v0[q], f);
 #pragma unroll
-            for (int i = 0; i < V::kN; ++i) acc[q][i] = fmaf(wj, f[i], acc[q][i]);
+            for (int i = 0; i < V::kN; ++i) acc[q][i] = fmaf(w0, f[i], acc[q][i]);
+          }
+          // a select rather than a branch, so the second row's loads are not sunk
+          // behind the first row's arithmetic
+#pragma unroll
+          for (int q = 0; q < kChunks; ++q) {
+            float f[V::kN];
+            V::load(v1[q], f);
+#pragma unroll
+            for (int i = 0; i < V::kN; ++i) {
+              const float t = fmaf(w1, f[i], acc[q][i]);
+              acc[q][i] = two ? t : acc[q][i];
+            }
           }
         }
       }
+      const __amdgpu_buffer_rsrc_t bd = make_rsrc(dst + c0, bytes);
 #pragma unroll
-      for (int q = 0; q < kChunks; ++q) {
-        const int c = c0 + q * kWave + lane;
-        if (c < row_vec) dst[c] = V::store(acc[q]);
-      }
+      for (int q = 0; q < kChunks; ++q)
+        buffer_store16(V::store(acc[q]), bd, static_cast<uint32_t>(q * kWave + lane) * 16u);
     }
   }
 }

@@ -19,7 +19,7 @@
 //                the rank among them is a popcount, and per-wave counts in LDS
 //                order the waves. Slot = chunk base + running count + rank, so
 //                the order inside an expert is the flat-pair order (stable).
-//   4. gather  : one wave per local row copies x[token] into x_perm with 16-byte
+//   4. gather  : one wave per part of a local row copies x[token] into x_perm with 16-byte
 //                loads and stores; the row count is read on the device.
 #include "moe_internal.h"
 
@@ -193,28 +193,36 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
   }
 }
 
+// Rows are copied in parts of kGatherVec 16-byte vectors (8 per lane), one part
+// per wave, so that a few long rows still spread over many waves and every lane
+// keeps 8 loads in flight.
+constexpr int kGatherPerLane = 8;
+constexpr int kGatherVec = kWave * kGatherPerLane;
+
 __global__ __launch_bounds__(kThreads) void dispatch_gather_kernel(
     const uint4* __restrict__ x, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ offsets, uint4* __restrict__ x_perm, int e_begin, int e_end, int k,
-    int row_vec, int n_max) {
+    int row_vec, int parts, int n_max) {
   const int seg0 = offsets[e_begin];
   // rows past n_max (only reachable when topk_idx repeats an id in a token) are dropped
   const int n_loc = min(offsets[e_end] - seg0, n_max);
   const int lane = lane_id();
   const int nwaves = gridDim.x * (kThreads / kWave);
-  for (int r = uniform(blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave); r < n_loc; r += nwaves) {
+  const int64_t items = static_cast<int64_t>(n_loc) * parts;
+  for (int64_t it = uniform(blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave); it < items; it += nwaves) {
+    const int r = static_cast<int>(it / parts);
+    const int c0 = static_cast<int>(it - static_cast<int64_t>(r) * parts) * kGatherVec;
     const int tok = uniform(perm[seg0 + r] / k);
-    const uint4* src = x + static_cast<int64_t>(tok) * row_vec;
-    uint4* dst = x_perm + static_cast<int64_t>(r) * row_vec;
-    int c = lane;
-    for (; c + 3 * kWave < row_vec; c += 4 * kWave) {
-      const uint4 a0 = src[c], a1 = src[c + kWave], a2 = src[c + 2 * kWave], a3 = src[c + 3 * kWave];
-      dst[c] = a0;
-      dst[c + kWave] = a1;
-      dst[c + 2 * kWave] = a2;
-      dst[c + 3 * kWave] = a3;
-    }
-    for (; c < row_vec; c += kWave) dst[c] = src[c];
+    // buffers over the part's vectors of this row: lanes past the row end load zero
+    // and their stores are dropped, with no branch between the loads
+    const uint32_t bytes = static_cast<uint32_t>(min(kGatherVec, row_vec - c0)) * 16u;
+    const __amdgpu_buffer_rsrc_t src = make_rsrc(x + static_cast<int64_t>(tok) * row_vec + c0, bytes);
+    const __amdgpu_buffer_rsrc_t dst = make_rsrc(x_perm + static_cast<int64_t>(r) * row_vec + c0, bytes);
+    uint4 v[kGatherPerLane];
+#pragma unroll
+    for (int i = 0; i < kGatherPerLane; ++i) v[i] = buffer_load16(src, static_cast<uint32_t>(i * kWave + lane) * 16u);
+#pragma unroll
+    for (int i = 0; i < kGatherPerLane; ++i) buffer_store16(v[i], dst, static_cast<uint32_t>(i * kWave + lane) * 16u);
   }
 }
 
@@ -253,13 +261,14 @@ hipError_t launch_dispatch(const void* x, size_t row_bytes, const int32_t* idx, 
   hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(n_chunks), dim3(kThreads), 0, stream, idx, bases,
                      offsets, perm, pair_pos, P, E, e_begin, e_end);
   const int row_vec = static_cast<int>(row_bytes / 16);
-  const int64_t waves_needed = n_max;  // one wave per row at most
+  const int parts = (row_vec + kGatherVec - 1) / kGatherVec;
+  const int64_t waves_needed = n_max * parts;  // one wave per row part at most
   int64_t blocks = (waves_needed + (kThreads / kWave) - 1) / (kThreads / kWave);
-  if (blocks > 2048) blocks = 2048;
+  if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(dispatch_gather_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
                      stream, static_cast<const uint4*>(x), perm, offsets, static_cast<uint4*>(x_perm),
-                     e_begin, e_end, k, row_vec, static_cast<int>(n_max));
+                     e_begin, e_end, k, row_vec, parts, static_cast<int>(n_max));
   return hipGetLastError();
 }
 

@@ -112,17 +112,6 @@ __device__ __forceinline__ T opaque(T v) {
 }
 
 // Raw buffer resource over [base, base + bytes): loads past the end return 0.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
-                                           0x00020000);
-}
-
-__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset) {
-  typedef int i32x4_t __attribute__((ext_vector_type(4)));
-  const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, static_cast<int>(voffset), 0, 0);
-  return make_uint4(static_cast<uint32_t>(v.x), static_cast<uint32_t>(v.y), static_cast<uint32_t>(v.z),
-                    static_cast<uint32_t>(v.w));
-}
 
 }  // namespace gemm
 }  // namespace moe

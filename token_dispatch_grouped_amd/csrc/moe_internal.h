@@ -30,6 +30,26 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 
 __device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) & (kWave - 1); }
 
+// Raw buffer resource over `bytes` bytes at `base`: loads past the end return
+// zero and stores past the end are dropped, with no branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset) {
+  const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, static_cast<int>(voffset), 0, 0);
+  return make_uint4(static_cast<uint32_t>(v.x), static_cast<uint32_t>(v.y), static_cast<uint32_t>(v.z),
+                    static_cast<uint32_t>(v.w));
+}
+
+__device__ __forceinline__ void buffer_store16(uint4 v, __amdgpu_buffer_rsrc_t rsrc, uint32_t voffset) {
+  const i32x4_t d = {static_cast<int>(v.x), static_cast<int>(v.y), static_cast<int>(v.z), static_cast<int>(v.w)};
+  __builtin_amdgcn_raw_buffer_store_b128(d, rsrc, static_cast<int>(voffset), 0, 0);
+}
+
 // Launchers (host side). Each returns hipSuccess or the launch error.
 hipError_t launch_route_topk(const float* logits, int32_t* idx, float* w, int64_t T, int E, int k,
                              hipStream_t stream);

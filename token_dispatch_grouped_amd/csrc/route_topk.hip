@@ -5,7 +5,7 @@
 // the k largest logits of each token in descending order, equal logits to the
 // lower expert id (signed zeros equal), and weights = softmax of those k logits.
 //
-// Design: G lanes (a power of two, G <= 64) share one token and each lane keeps
+// Design: G lanes (a power of two, G <= 32) share one token and each lane keeps
 // VPL logits in registers, expert e = g + v*G, so a group's loads are contiguous.
 // A logit and its id form one 64-bit key (order-preserving float bits << 32 |
 // ~id), so "larger value, then lower id" is a plain unsigned max and every key
@@ -148,18 +148,21 @@ hipError_t launch_g(const float* logits, int32_t* idx, float* w, int64_t T, int 
 hipError_t launch_route_topk(const float* logits, int32_t* idx, float* w, int64_t T, int E, int k,
                              hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  // group size G = next power of two >= E, capped at a wave; VPL = values per lane
+  // G lanes per token, VPL logits per lane (G * VPL >= E). Per token, a round costs
+  // about G * (c1 * VPL + c2 * log2 G) lane-slots: the per-lane scan grows with VPL,
+  // the group maximum with G log G, so small experts counts take one lane per
+  // expert and larger ones 8-32 lanes with more logits each.
   if (E <= 1) return launch_g<1, 1>(logits, idx, w, T, E, k, stream);
   if (E <= 2) return launch_g<2, 1>(logits, idx, w, T, E, k, stream);
   if (E <= 4) return launch_g<4, 1>(logits, idx, w, T, E, k, stream);
   if (E <= 8) return launch_g<8, 1>(logits, idx, w, T, E, k, stream);
-  if (E <= 16) return launch_g<16, 1>(logits, idx, w, T, E, k, stream);
-  if (E <= 32) return launch_g<32, 1>(logits, idx, w, T, E, k, stream);
-  if (E <= 64) return launch_g<64, 1>(logits, idx, w, T, E, k, stream);
-  if (E <= 128) return launch_g<64, 2>(logits, idx, w, T, E, k, stream);
-  if (E <= 256) return launch_g<64, 4>(logits, idx, w, T, E, k, stream);
-  if (E <= 512) return launch_g<64, 8>(logits, idx, w, T, E, k, stream);
-  return launch_g<64, 16>(logits, idx, w, T, E, k, stream);
+  if (E <= 16) return launch_g<8, 2>(logits, idx, w, T, E, k, stream);
+  if (E <= 32) return launch_g<8, 4>(logits, idx, w, T, E, k, stream);
+  if (E <= 64) return launch_g<8, 8>(logits, idx, w, T, E, k, stream);
+  if (E <= 128) return launch_g<16, 8>(logits, idx, w, T, E, k, stream);
+  if (E <= 256) return launch_g<16, 16>(logits, idx, w, T, E, k, stream);
+  if (E <= 512) return launch_g<16, 32>(logits, idx, w, T, E, k, stream);
+  return launch_g<32, 32>(logits, idx, w, T, E, k, stream);
 }
 
 }  // namespace moe
