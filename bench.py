@@ -133,6 +133,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dense8", choices=sorted(mi.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", choices=["fused", "staged"], default="fused",
+                    help="fused: dispatch indices only, the gate/up GEMM gathers rows from x; "
+                         "staged: dispatch gathers rows into x_perm first")
     ap.add_argument("--clock-seconds", type=float, default=0.0,
                     help="after timing, repeat the step for this many seconds while sampling the "
                          "shader clock with rocm-smi; reports the median as sclk_mhz")
@@ -179,7 +182,8 @@ def main() -> int:
     # every buffer the step writes, allocated once
     idx = torch.empty((w.T, w.k), dtype=torch.int32, device=dev)
     wts = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
-    disp = moe.dispatch_alloc(dx, w.k, w.E, w.e_begin, w.e_end)
+    fused = args.path == "fused"
+    disp = moe.dispatch_alloc(dx, w.k, w.E, w.e_begin, w.e_end, gather=not fused)
     h = torch.empty((w.n_max, w.d_ff), dtype=dx.dtype, device=dev)
     y = torch.empty((w.n_max, w.d), dtype=dx.dtype, device=dev)
     out = torch.empty((w.T, w.d), dtype=dx.dtype, device=dev)
@@ -187,13 +191,20 @@ def main() -> int:
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
 
+    def gemm():
+        if fused:
+            moe.grouped_gemm_gather(dx, disp.perm, disp.offsets, dgu, ddn, w.k, w.E, w.e_begin, w.e_end,
+                                    h=h, y=y, stream=stream)
+        else:
+            moe.grouped_gemm(disp.x_perm, disp.offsets, dgu, ddn, w.T, w.k, w.E, w.e_begin, w.e_end,
+                             h=h, y=y, stream=stream)
+
     def step(i=None):
         moe.route_topk(dl, w.k, idx, wts, stream=stream)
-        moe.dispatch(dx, idx, w.E, w.e_begin, w.e_end, out=disp, stream=stream)
+        moe.dispatch(dx, idx, w.E, w.e_begin, w.e_end, out=disp, stream=stream, gather=not fused)
         if i is not None:
             ev[i][0].record(stream)
-        moe.grouped_gemm(disp.x_perm, disp.offsets, dgu, ddn, w.T, w.k, w.E, w.e_begin, w.e_end,
-                         h=h, y=y, stream=stream)
+        gemm()
         if i is not None:
             ev[i][1].record(stream)
         moe.combine(y, disp.pair_pos, wts, w.T, w.k, w.E, w.e_begin, w.e_end, out=out, stream=stream)
@@ -216,7 +227,8 @@ def main() -> int:
 
     flops = 6.0 * n_loc * w.d * w.d_ff  # gate/up (4 N d d_ff) + down (2 N d d_ff)
     b = 2 if w.dtype == "bf16" else 4
-    # weights of every active local expert once, x_perm and H read once, H and Y written once
+    # weights of every active local expert once, one activation row per local pair and H read
+    # once, H and Y written once
     gemm_bytes = 3.0 * active * w.d * w.d_ff * b + 2.0 * n_loc * (w.d + w.d_ff) * b
     peak_flops = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
     t_gemm = gemm_ms * 1e-3
@@ -227,7 +239,8 @@ def main() -> int:
         bound = "mfma" if w.dtype == "bf16" else "alu"
         achieved, peak, unit = flops / t_gemm / 1e12, peak_flops, "TFLOP/s"
     roofline = {
-        "kernel": "moe_grouped_gemm (gate/up+SwiGLU launch, then down launch)",
+        "kernel": ("moe_grouped_gemm_gather" if fused else "moe_grouped_gemm")
+                  + " (gate/up+SwiGLU launch, then down launch)",
         "bound": bound,
         "achieved": round(achieved, 2),
         "peak": peak,
@@ -253,7 +266,7 @@ def main() -> int:
         "data": "synthetic (seeded normal draws; see moe_inputs)",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "d_ff": w.d_ff, "E": w.E, "k": w.k,
                    "local_experts": [w.e_begin, w.e_end], "N_loc": n_loc, "active_local_experts": active,
-                   "parallelism": "one rank's share on 1 GPU"},
+                   "parallelism": "one rank's share on 1 GPU", "path": args.path},
         "local_pairs_per_s": round(n_loc / (ms_step * 1e-3), 1),
         "roofline": roofline,
         "cpu_baseline": None,
@@ -265,10 +278,9 @@ def main() -> int:
         e[0].record(stream)
         moe.route_topk(dl, w.k, idx, wts, stream=stream)
         e[1].record(stream)
-        moe.dispatch(dx, idx, w.E, w.e_begin, w.e_end, out=disp, stream=stream)
+        moe.dispatch(dx, idx, w.E, w.e_begin, w.e_end, out=disp, stream=stream, gather=not fused)
         e[2].record(stream)
-        moe.grouped_gemm(disp.x_perm, disp.offsets, dgu, ddn, w.T, w.k, w.E, w.e_begin, w.e_end,
-                         h=h, y=y, stream=stream)
+        gemm()
         e[3].record(stream)
         moe.combine(y, disp.pair_pos, wts, w.T, w.k, w.E, w.e_begin, w.e_end, out=out, stream=stream)
         e[4].record(stream)

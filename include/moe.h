@@ -117,6 +117,15 @@ moe_status moe_dispatch(const moe_shape* s, moe_dtype dt, const void* x,
                         int32_t* perm, int32_t* pair_pos, void* x_perm,
                         void* workspace, hipStream_t stream);
 
+/* moe_dispatch without the row gather: counts, offsets, perm and pair_pos as
+ * moe_dispatch writes them, and no x_perm. For the fused path, in which
+ * moe_grouped_gemm_gather reads each local row straight from x. Same sources,
+ * arguments and errors as moe_dispatch (x, x_perm and dt are not taken); the
+ * workspace size is moe_dispatch_workspace_bytes(s). */
+moe_status moe_dispatch_indices(const moe_shape* s, const int32_t* topk_idx,
+                                int32_t* counts, int32_t* offsets, int32_t* perm,
+                                int32_t* pair_pos, void* workspace, hipStream_t stream);
+
 /* Bytes of device workspace moe_grouped_gemm needs for this shape (may be 0). */
 size_t moe_grouped_gemm_workspace_bytes(const moe_shape* s, moe_dtype dt);
 
@@ -141,6 +150,21 @@ moe_status moe_grouped_gemm(const moe_shape* s, moe_dtype dt, const void* x_perm
                             const int32_t* offsets, const void* w_gate_up,
                             const void* w_down, void* h, void* y, void* workspace,
                             hipStream_t stream);
+
+/* moe_grouped_gemm with the dispatch's row gather folded into the gate/up
+ * loads: the activation rows of local row r are x[perm[offsets[e_begin] + r] / k]
+ * read directly from x, so x_perm is never written or read. Results (h, y) are
+ * bit-identical to moe_dispatch + moe_grouped_gemm. Same sources as those two.
+ *   x         [T, d] dt, read only: hidden states.
+ *   perm      [T*k] int32 DEVICE array from moe_dispatch or moe_dispatch_indices.
+ *   offsets, w_gate_up, w_down, h, y, workspace: as for moe_grouped_gemm
+ *             (workspace size moe_grouped_gemm_workspace_bytes(s, dt)).
+ * MOE_EUNSUPPORTED unless dt = MOE_BF16, d and d_ff are multiples of 32 and
+ * T * d * 2 bytes fit in 31 bits; use moe_dispatch + moe_grouped_gemm then. */
+moe_status moe_grouped_gemm_gather(const moe_shape* s, moe_dtype dt, const void* x,
+                                   const int32_t* perm, const int32_t* offsets,
+                                   const void* w_gate_up, const void* w_down, void* h,
+                                   void* y, void* workspace, hipStream_t stream);
 
 /* Weighted combine back to token order ([EP] "Despacho de tokens": results are
  * combined with the routing weights; "Adicionando uma implementação": the

@@ -123,3 +123,37 @@ def test_zero_tokens_is_a_no_op_on_the_host():
     assert _route(s, logits=NULL, idx=NULL, w=NULL) == moe.MOE_OK
     assert _gemm(s, ptrs=[NULL] * 6) == moe.MOE_OK
     assert _combine(s, ptrs=[NULL] * 4) == moe.MOE_OK
+
+
+def _dispatch_indices(s, ptrs=None):
+    p = ptrs or [FAKE] * 5
+    return moe.lib().moe_dispatch_indices(ctypes.byref(s), p[0], p[1], p[2], p[3], p[4], FAKE, NULL)
+
+
+def _gemm_gather(s, dt=moe.MOE_BF16, ptrs=None):
+    p = ptrs or [FAKE] * 7
+    return moe.lib().moe_grouped_gemm_gather(ctypes.byref(s), dt, p[0], p[1], p[2], p[3], p[4], p[5], p[6],
+                                             NULL, NULL)
+
+
+def test_fused_path_entry_points_validate_on_the_host():
+    s = _shape()
+    for i in range(5):
+        p = [FAKE] * 5
+        p[i] = NULL
+        assert _dispatch_indices(s, ptrs=p) == moe.MOE_EINVAL, i
+    for i in range(7):
+        p = [FAKE] * 7
+        p[i] = NULL
+        assert _gemm_gather(s, ptrs=p) == moe.MOE_EINVAL, i
+    assert _dispatch_indices(_shape(k=0)) == moe.MOE_EINVAL
+    assert _gemm_gather(_shape(d=12)) == moe.MOE_EINVAL
+    assert _gemm_gather(s, dt=7) == moe.MOE_EINVAL
+    # the row gather lives only in the pipelined bf16 kernel
+    assert _gemm_gather(s, dt=moe.MOE_F32) == moe.MOE_EUNSUPPORTED
+    assert _gemm_gather(_shape(d=72)) == moe.MOE_EUNSUPPORTED
+    assert _gemm_gather(_shape(d_ff=40)) == moe.MOE_EUNSUPPORTED
+    # x is addressed with 32-bit offsets: T * d * 2 bytes must stay below 2^31
+    assert _gemm_gather(_shape(T=2**20, d=1024, k=1)) == moe.MOE_EUNSUPPORTED
+    # T = 0: nothing is enqueued
+    assert _gemm_gather(_shape(T=0), ptrs=[NULL] * 7) == moe.MOE_OK

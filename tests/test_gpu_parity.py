@@ -256,3 +256,57 @@ def test_layer_register_staged_kernel(w, monkeypatch):
     shapes the pipelined kernel would otherwise take."""
     monkeypatch.setenv("MOE_GEMM_KERNEL", "regs")
     _layer_case(w)
+
+
+# ----------------------------------------------------------------------------- fused path (row gather in the GEMM loads)
+
+FUSED = [SMALL[3], SMALL[4], SMALL[5],
+         mi.Workload("fused_ragged_experts", 1100, 256, 160, 24, 3, 4, 20, "bf16", 25),
+         mi.Workload("fused_partial_range", 640, 192, 128, 16, 4, 6, 10, "bf16", 26)]
+
+
+@pytest.mark.parametrize("w", FUSED, ids=[w.name for w in FUSED])
+def test_fused_layer_matches_oracle_and_staged_path(w):
+    """moe_dispatch_indices + moe_grouped_gemm_gather: the oracle's result, and
+    bit for bit the staged path's H, Y and output."""
+    res, ref = _layer_case(w)
+    logits = mi.router_logits(w)
+    x = mi.hidden_states(w)
+    wgu, wdn = mi.expert_weights(w)
+    fused = moe.layer(g.to_dev(x, w.dtype), g.to_dev(logits, "f32"), g.to_dev(wgu, w.dtype),
+                      g.to_dev(wdn, w.dtype), w.k, w.e_begin, w.e_end, fused=True)
+    torch.cuda.synchronize()
+    assert fused["x_perm"] is None
+    n_loc = ref["x_perm"].shape[0]
+    for key in ("idx", "counts", "offsets", "perm", "pair_pos"):
+        assert torch.equal(fused[key], res[key]), key
+    assert torch.equal(fused["h"][:n_loc], res["h"][:n_loc])
+    assert torch.equal(fused["y"][:n_loc], res["y"][:n_loc])
+    assert torch.equal(fused["out"], res["out"])
+
+
+def test_fused_layer_every_tile_height():
+    counts = [0, 1, 31, 32, 33, 64, 65, 128, 129, 255, 256, 257, 288, 289, 300, 513, 544]
+    E = len(counts)
+    w = mi.Workload("fused_tile_heights", int(sum(counts)), 256, 160, E, 1, 0, E, "bf16", 27)
+    logits = _one_hot_logits(counts, E, 27)
+    res, ref = _layer_case(w, logits)
+    x = mi.hidden_states(w)
+    wgu, wdn = mi.expert_weights(w)
+    fused = moe.layer(g.to_dev(x, w.dtype), g.to_dev(logits, "f32"), g.to_dev(wgu, w.dtype),
+                      g.to_dev(wdn, w.dtype), w.k, w.e_begin, w.e_end, fused=True)
+    torch.cuda.synchronize()
+    n_loc = ref["x_perm"].shape[0]
+    assert torch.equal(fused["h"][:n_loc], res["h"][:n_loc])
+    assert torch.equal(fused["out"], res["out"])
+
+
+def test_fused_gemm_rejects_unsupported_shapes():
+    w = SMALL[7]  # fp32
+    x = torch.zeros((w.T, w.d), dtype=torch.float32, device="cuda")
+    logits = torch.zeros((w.T, w.E), dtype=torch.float32, device="cuda")
+    wgu = torch.zeros((w.E_loc, w.d, 2 * w.d_ff), dtype=torch.float32, device="cuda")
+    wdn = torch.zeros((w.E_loc, w.d_ff, w.d), dtype=torch.float32, device="cuda")
+    with pytest.raises(moe.MoeError) as e:
+        moe.layer(x, logits, wgu, wdn, w.k, w.e_begin, w.e_end, fused=True)
+    assert e.value.status == moe.MOE_EUNSUPPORTED

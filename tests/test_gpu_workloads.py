@@ -5,7 +5,8 @@ Top-k ids, counts, offsets, the permutation and pair positions are checked in
 full against the oracle; gathered rows, expert outputs and layer outputs on
 samples the oracle computes one by one (rows of x_perm, rows of Y through their
 expert's FFN, tokens through oracle.token_outputs, including tokens with no
-local pair).
+local pair). The fused path (moe_dispatch_indices + moe_grouped_gemm_gather)
+must reproduce the staged path's Y and output bit for bit.
 """
 import numpy as np
 import pytest
@@ -39,6 +40,15 @@ def test_full_workload_sampled(name):
     res = moe.layer(dx, dl, dgu, ddn, w.k, w.e_begin, w.e_end)
     torch.cuda.synchronize()
     print("  device layer done", flush=True)
+    if w.dtype == "bf16":
+        # the fused path (row gather in the GEMM loads) gives the same bits
+        fused = moe.layer(dx, dl, dgu, ddn, w.k, w.e_begin, w.e_end, fused=True)
+        torch.cuda.synchronize()
+        n = int(res["offsets"][w.e_end].item() - res["offsets"][w.e_begin].item())
+        assert torch.equal(fused["y"][:n], res["y"][:n])
+        assert torch.equal(fused["out"], res["out"])
+        del fused
+        print("  fused path bit-identical", flush=True)
     del dgu, ddn
 
     # routing and dispatch in full

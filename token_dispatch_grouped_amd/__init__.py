@@ -58,6 +58,8 @@ def _load():
             "moe_route_topk": (ctypes.c_int, [S, P, P, P, P]),
             "moe_dispatch_workspace_bytes": (SZ, [S]),
             "moe_dispatch": (ctypes.c_int, [S, ctypes.c_int, P, P, P, P, P, P, P, P, P]),
+            "moe_dispatch_indices": (ctypes.c_int, [S, P, P, P, P, P, P, P]),
+            "moe_grouped_gemm_gather": (ctypes.c_int, [S, ctypes.c_int, P, P, P, P, P, P, P, P, P]),
             "moe_grouped_gemm_workspace_bytes": (SZ, [S, ctypes.c_int]),
             "moe_grouped_gemm": (ctypes.c_int, [S, ctypes.c_int, P, P, P, P, P, P, P, P]),
             "moe_combine": (ctypes.c_int, [S, ctypes.c_int, P, P, P, P, P]),
@@ -171,8 +173,9 @@ class Dispatch:
     workspace: object
 
 
-def dispatch_alloc(x, k: int, E: int, e_begin: int, e_end: int) -> Dispatch:
-    """Allocate every dispatch output (sized on the host, no device read)."""
+def dispatch_alloc(x, k: int, E: int, e_begin: int, e_end: int, gather: bool = True) -> Dispatch:
+    """Allocate every dispatch output (sized on the host, no device read); without
+    `gather` there is no x_perm (the fused path reads rows straight from x)."""
     torch = _torch()
     T, d = x.shape
     n_max = T * min(k, e_end - e_begin)
@@ -184,22 +187,31 @@ def dispatch_alloc(x, k: int, E: int, e_begin: int, e_end: int) -> Dispatch:
         offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
         perm=torch.empty(T * k, dtype=torch.int32, device=dev),
         pair_pos=torch.empty(T * k, dtype=torch.int32, device=dev),
-        x_perm=torch.empty((n_max, d), dtype=x.dtype, device=dev),
+        x_perm=torch.empty((n_max, d), dtype=x.dtype, device=dev) if gather else None,
         workspace=torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev),
     )
 
 
-def dispatch(x, topk_idx, E: int, e_begin: int, e_end: int, out: Dispatch | None = None, stream=None) -> Dispatch:
-    """Histogram, offsets, stable permutation and local-row gather."""
+def dispatch(x, topk_idx, E: int, e_begin: int, e_end: int, out: Dispatch | None = None, stream=None,
+             gather: bool = True) -> Dispatch:
+    """Histogram, offsets, stable permutation and (with `gather`) the local-row
+    gather into x_perm; without it, moe_dispatch_indices (no x_perm)."""
     _dev(x, topk_idx)
     T, d = x.shape
     k = topk_idx.shape[1] if topk_idx.dim() == 2 else 1
     if out is None:
-        out = dispatch_alloc(x, k, E, e_begin, e_end)
+        out = dispatch_alloc(x, k, E, e_begin, e_end, gather=gather)
     s = shape(T, d, 8, E, k, e_begin, e_end)
-    _check(_load().moe_dispatch(ctypes.byref(s), _dtype_code(x), _ptr(x), _ptr(topk_idx), _ptr(out.counts),
-                                _ptr(out.offsets), _ptr(out.perm), _ptr(out.pair_pos), _ptr(out.x_perm),
-                                _ptr(out.workspace), _stream(stream)), "moe_dispatch")
+    if gather:
+        if out.x_perm is None:
+            raise ValueError("this Dispatch has no x_perm; allocate it with gather=True")
+        _check(_load().moe_dispatch(ctypes.byref(s), _dtype_code(x), _ptr(x), _ptr(topk_idx), _ptr(out.counts),
+                                    _ptr(out.offsets), _ptr(out.perm), _ptr(out.pair_pos), _ptr(out.x_perm),
+                                    _ptr(out.workspace), _stream(stream)), "moe_dispatch")
+    else:
+        _check(_load().moe_dispatch_indices(ctypes.byref(s), _ptr(topk_idx), _ptr(out.counts), _ptr(out.offsets),
+                                            _ptr(out.perm), _ptr(out.pair_pos), _ptr(out.workspace),
+                                            _stream(stream)), "moe_dispatch_indices")
     return out
 
 
@@ -229,6 +241,35 @@ def grouped_gemm(x_perm, offsets, w_gate_up, w_down, T: int, k: int, E: int, e_b
     return h, y
 
 
+def grouped_gemm_gather(x, perm, offsets, w_gate_up, w_down, k: int, E: int, e_begin: int, e_end: int,
+                        h=None, y=None, stream=None):
+    """grouped_gemm reading each local row straight from x through perm (no
+    x_perm): returns (h [N_max, d_ff], y [N_max, d]), bit-identical to
+    dispatch + grouped_gemm."""
+    torch = _torch()
+    _dev(x, perm, offsets, w_gate_up, w_down)
+    T, d = x.shape
+    e_loc, d_ff, _ = w_down.shape
+    if w_gate_up.shape != (e_loc, d, 2 * d_ff) or w_down.shape != (e_loc, d_ff, d):
+        raise ValueError("w_gate_up must be [E_loc, d, 2*d_ff] and w_down [E_loc, d_ff, d]")
+    if e_loc != e_end - e_begin:
+        raise ValueError("expert weights must hold exactly the local experts")
+    n_max = T * min(k, e_loc)
+    if h is None:
+        h = torch.empty((n_max, d_ff), dtype=x.dtype, device=x.device)
+    if y is None:
+        y = torch.empty((n_max, d), dtype=x.dtype, device=x.device)
+    _dev(h, y)
+    s = shape(T, d, d_ff, E, k, e_begin, e_end)
+    dt = _dtype_code(x)
+    ws_bytes = _load().moe_grouped_gemm_workspace_bytes(ctypes.byref(s), dt)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device) if ws_bytes else None
+    _check(_load().moe_grouped_gemm_gather(ctypes.byref(s), dt, _ptr(x), _ptr(perm), _ptr(offsets),
+                                           _ptr(w_gate_up), _ptr(w_down), _ptr(h), _ptr(y), _ptr(ws),
+                                           _stream(stream)), "moe_grouped_gemm_gather")
+    return h, y
+
+
 def combine(y, pair_pos, topk_w, T: int, k: int, E: int, e_begin: int, e_end: int, out=None, stream=None):
     """out[t] = sum_j topk_w[t, j] * y[pair_pos[t*k + j]] over local pairs; [T, d]."""
     torch = _torch()
@@ -243,13 +284,18 @@ def combine(y, pair_pos, topk_w, T: int, k: int, E: int, e_begin: int, e_end: in
     return out
 
 
-def layer(x, logits, w_gate_up, w_down, k: int, e_begin: int, e_end: int, stream=None) -> dict:
-    """The whole forward of one rank: route -> dispatch -> grouped GEMM -> combine."""
+def layer(x, logits, w_gate_up, w_down, k: int, e_begin: int, e_end: int, stream=None, fused: bool = False) -> dict:
+    """The whole forward of one rank: route -> dispatch -> grouped GEMM -> combine.
+    With `fused`, the dispatch writes indices only and the GEMM gathers the rows."""
     T = x.shape[0]
     E = logits.shape[1]
     idx, w = route_topk(logits, k, stream=stream)
-    disp = dispatch(x, idx, E, e_begin, e_end, stream=stream)
-    h, y = grouped_gemm(disp.x_perm, disp.offsets, w_gate_up, w_down, T, k, E, e_begin, e_end, stream=stream)
+    disp = dispatch(x, idx, E, e_begin, e_end, stream=stream, gather=not fused)
+    if fused:
+        h, y = grouped_gemm_gather(x, disp.perm, disp.offsets, w_gate_up, w_down, k, E, e_begin, e_end,
+                                   stream=stream)
+    else:
+        h, y = grouped_gemm(disp.x_perm, disp.offsets, w_gate_up, w_down, T, k, E, e_begin, e_end, stream=stream)
     out = combine(y, disp.pair_pos, w, T, k, E, e_begin, e_end, stream=stream)
     return dict(idx=idx, w=w, counts=disp.counts, offsets=disp.offsets, perm=disp.perm,
                 pair_pos=disp.pair_pos, x_perm=disp.x_perm, h=h, y=y, out=out)

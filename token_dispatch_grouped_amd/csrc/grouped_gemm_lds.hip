@@ -154,10 +154,20 @@ struct Layout {
   static_assert(XR == 0 || (XR == 1 && WM == 2), "one shared extra row block, two waves along M");
 };
 
-template <bool SWIGLU, int H>
+// Where activation rows come from: rows of A in order (x_perm, H), or, with
+// GATHER, row r of the local segment is row perm_seg[r] / k of A (the token's
+// hidden state in x, the row gather of the dispatch done by the loads).
+struct ARows {
+  const int32_t* perm_seg;  // perm + offsets[e_begin]
+  int k;
+  uint32_t a_bytes;         // bytes of A (T * K * 2)
+};
+
+template <bool SWIGLU, bool GATHER, int H>
 __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __restrict__ A,
                                           const uint16_t* __restrict__ Bexp, uint16_t* __restrict__ C,
-                                          int row0, int rows_valid, int n0, int K, int N, int ldb) {
+                                          int row0, int rows_valid, int n0, int K, int N, int ldb,
+                                          const ARows& ar) {
   using L = Layout<H>;
   constexpr int MI = L::MI, NI = L::NI, WM = L::WM, WN = L::WN, PER = L::PER;
   const int tid = threadIdx.x;
@@ -174,8 +184,9 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
   // logical chunk (L & 3) ^ ((row >> 2) & 3) into LDS slot L. Slots beyond the
   // A_INSTR instructions repeat an earlier instruction (identical bytes to the same
   // place), so every wave issues PER loads per stage.
-  const uint16_t* a_tile = A + static_cast<int64_t>(row0) * K;
-  const uint32_t a_bytes = static_cast<uint32_t>(rows_valid) * static_cast<uint32_t>(K) * 2u;
+  const uint16_t* a_tile = GATHER ? A : A + static_cast<int64_t>(row0) * K;
+  const uint32_t a_bytes =
+      GATHER ? ar.a_bytes : static_cast<uint32_t>(rows_valid) * static_cast<uint32_t>(K) * 2u;
   const uint32_t b_bytes = static_cast<uint32_t>(K) * static_cast<uint32_t>(ldb) * 2u;
   uint32_t a_voff[L::A_PER_WAVE];
   int a_slot[L::A_PER_WAVE];
@@ -185,7 +196,14 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
     a_slot[jj] = j;
     const int r = 16 * j + (lane >> 2);
     const int c = (lane & 3) ^ ((lane >> 4) & 3);
-    a_voff[jj] = static_cast<uint32_t>(r) * static_cast<uint32_t>(K) * 2u + static_cast<uint32_t>(c) * 16u;
+    if (GATHER) {
+      // the token's row; rows past the tile's valid rows point past the buffer (zeros)
+      const uint32_t src = r < rows_valid ? static_cast<uint32_t>(ar.perm_seg[row0 + r] / ar.k) * static_cast<uint32_t>(K) * 2u
+                                          : 0x80000000u;
+      a_voff[jj] = src + static_cast<uint32_t>(c) * 16u;
+    } else {
+      a_voff[jj] = static_cast<uint32_t>(r) * static_cast<uint32_t>(K) * 2u + static_cast<uint32_t>(c) * 16u;
+    }
   }
   // Weight instruction j covers k-rows 2j, 2j+1 of the stage: lane L brings k-row
   // 2j + L/32, logical chunk (L & 31) ^ (4 * (k & 3)) (8 columns) into LDS slot L.
@@ -429,10 +447,11 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
   }
 }
 
-template <bool SWIGLU>
+template <bool SWIGLU, bool GATHER>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_lds_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
-    const int32_t* __restrict__ offsets, int e_begin, int e_loc, int K, int N, int ldb, int n_max) {
+    const int32_t* __restrict__ offsets, int e_begin, int e_loc, int K, int N, int ldb, int n_max,
+    const int32_t* __restrict__ perm, int k, uint32_t a_bytes) {
   __shared__ __attribute__((aligned(1024))) uint16_t smem[kStages * (kAStageElems + kBStageElems)];
   __shared__ TileMap tm;
   // a remainder of at most 32 rows rides on the expert's last full tile (288 rows)
@@ -442,6 +461,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_lds_kernel(
   const int n_tiles = (N + kOutCols - 1) / kOutCols;
   const int total = uniform(tm.mstart[e_loc]) * n_tiles;
   const int64_t b_expert = static_cast<int64_t>(K) * ldb;
+  ARows ar{nullptr, k, a_bytes};
+  if (GATHER) ar.perm_seg = perm + offsets[e_begin];
 
   for (int tile = xcd_remap(blockIdx.x, gridDim.x); tile < total; tile += gridDim.x) {
     const TileCoord tc = find_tile(tm, tile, n_tiles, e_loc);
@@ -452,15 +473,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_lds_kernel(
     const int n0 = tc.nt * kOutCols;
     const uint16_t* Bexp = B + static_cast<int64_t>(tc.e) * b_expert;
     if (rows_valid > 256)
-      gemm_tile<SWIGLU, 288>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb);
+      gemm_tile<SWIGLU, GATHER, 288>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb, ar);
     else if (rows_valid > 128)
-      gemm_tile<SWIGLU, 256>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb);
+      gemm_tile<SWIGLU, GATHER, 256>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb, ar);
     else if (rows_valid > 64)
-      gemm_tile<SWIGLU, 128>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb);
+      gemm_tile<SWIGLU, GATHER, 128>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb, ar);
     else if (rows_valid > 32)
-      gemm_tile<SWIGLU, 64>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb);
+      gemm_tile<SWIGLU, GATHER, 64>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb, ar);
     else
-      gemm_tile<SWIGLU, 32>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb);
+      gemm_tile<SWIGLU, GATHER, 32>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb, ar);
     // every wave has waited for its last LDS reads; the next tile's loads may land
     __builtin_amdgcn_s_barrier();
   }
@@ -468,17 +489,26 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_lds_kernel(
 
 }  // namespace
 
-hipError_t launch_grouped_gemm_lds(const void* x_perm, const int32_t* offsets, const void* w_gu,
-                                   const void* w_dn, void* h, void* y, int d, int d_ff, int e_begin,
-                                   int e_loc, int64_t n_max, int grid_gate_up, int grid_down,
+hipError_t launch_grouped_gemm_lds(const void* a, const int32_t* perm, int64_t T, int k, const int32_t* offsets,
+                                   const void* w_gu, const void* w_dn, void* h, void* y, int d, int d_ff,
+                                   int e_begin, int e_loc, int64_t n_max, int grid_gate_up, int grid_down,
                                    hipStream_t stream) {
-  hipLaunchKernelGGL(grouped_gemm_lds_kernel<true>, dim3(grid_gate_up), dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t*>(x_perm), static_cast<const uint16_t*>(w_gu),
-                     static_cast<uint16_t*>(h), offsets, e_begin, e_loc, d, d_ff, 2 * d_ff,
-                     static_cast<int>(n_max));
-  hipLaunchKernelGGL(grouped_gemm_lds_kernel<false>, dim3(grid_down), dim3(kThreads), 0, stream,
+  if (perm != nullptr) {  // activation rows gathered from x by perm
+    const uint32_t a_bytes = static_cast<uint32_t>(T * d * 2);
+    hipLaunchKernelGGL((grouped_gemm_lds_kernel<true, true>), dim3(grid_gate_up), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(w_gu),
+                       static_cast<uint16_t*>(h), offsets, e_begin, e_loc, d, d_ff, 2 * d_ff,
+                       static_cast<int>(n_max), perm, k, a_bytes);
+  } else {
+    hipLaunchKernelGGL((grouped_gemm_lds_kernel<true, false>), dim3(grid_gate_up), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(w_gu),
+                       static_cast<uint16_t*>(h), offsets, e_begin, e_loc, d, d_ff, 2 * d_ff,
+                       static_cast<int>(n_max), nullptr, k, 0u);
+  }
+  hipLaunchKernelGGL((grouped_gemm_lds_kernel<false, false>), dim3(grid_down), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_dn),
-                     static_cast<uint16_t*>(y), offsets, e_begin, e_loc, d_ff, d, d, static_cast<int>(n_max));
+                     static_cast<uint16_t*>(y), offsets, e_begin, e_loc, d_ff, d, d, static_cast<int>(n_max),
+                     nullptr, k, 0u);
   return hipGetLastError();
 }
 

@@ -91,6 +91,19 @@ moe_status moe_dispatch(const moe_shape* s, moe_dtype dt, const void* x, const i
                                        s->e_begin, s->e_end, n_max_of(s), stream));
 }
 
+moe_status moe_dispatch_indices(const moe_shape* s, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                                int32_t* perm, int32_t* pair_pos, void* workspace, hipStream_t stream) {
+  const moe_status st = check_shape(s, true);
+  if (st != MOE_OK) return st;
+  if (counts == nullptr || offsets == nullptr) return MOE_EINVAL;
+  if (s->T > 0) {
+    if (topk_idx == nullptr || perm == nullptr || pair_pos == nullptr) return MOE_EINVAL;
+    if (moe::dispatch_workspace_bytes(s->T, s->k, s->E) > 0 && workspace == nullptr) return MOE_EINVAL;
+  }
+  return from_hip(moe::launch_dispatch(nullptr, 0, topk_idx, counts, offsets, perm, pair_pos, nullptr, workspace,
+                                       s->T, s->k, s->E, s->e_begin, s->e_end, n_max_of(s), stream));
+}
+
 size_t moe_grouped_gemm_workspace_bytes(const moe_shape* s, moe_dtype dt) {
   (void)s;
   (void)dt;
@@ -124,6 +137,29 @@ moe_status moe_grouped_gemm(const moe_shape* s, moe_dtype dt, const void* x_perm
       static_cast<const float*>(x_perm), offsets, static_cast<const float*>(w_gate_up),
       static_cast<const float*>(w_down), static_cast<float*>(h), static_cast<float*>(y), s->d, s->d_ff,
       s->e_begin, e_loc, n_max, stream));
+}
+
+moe_status moe_grouped_gemm_gather(const moe_shape* s, moe_dtype dt, const void* x, const int32_t* perm,
+                                   const int32_t* offsets, const void* w_gate_up, const void* w_down, void* h,
+                                   void* y, void* workspace, hipStream_t stream) {
+  (void)workspace;
+  const moe_status st = check_shape(s, true);
+  if (st != MOE_OK) return st;
+  if (!valid_dtype(dt)) return MOE_EINVAL;
+  if (s->T == 0) return MOE_OK;
+  if (x == nullptr || perm == nullptr || offsets == nullptr || w_gate_up == nullptr || w_down == nullptr ||
+      h == nullptr || y == nullptr)
+    return MOE_EINVAL;
+  // Only the pipelined bf16 kernel gathers rows in its loads: K in whole 32-wide
+  // stages, and x addressed through 32-bit buffer offsets.
+  if (dt != MOE_BF16 || s->d % 32 != 0 || s->d_ff % 32 != 0) return MOE_EUNSUPPORTED;
+  if (s->T * static_cast<int64_t>(s->d) * 2 + 64 > INT32_MAX) return MOE_EUNSUPPORTED;
+  if ((static_cast<int64_t>(s->d) + 64) * 2 * s->d_ff * 2 > INT32_MAX ||
+      (static_cast<int64_t>(s->d_ff) + 64) * s->d * 2 > INT32_MAX)
+    return MOE_EUNSUPPORTED;
+  return from_hip(moe::launch_grouped_gemm_gather(x, perm, offsets, w_gate_up, w_down, h, y, s->d, s->d_ff,
+                                                  s->e_begin, s->e_end - s->e_begin, n_max_of(s), s->T, s->k,
+                                                  stream));
 }
 
 moe_status moe_combine(const moe_shape* s, moe_dtype dt, const void* y, const int32_t* pair_pos,
