@@ -136,6 +136,9 @@ def main() -> int:
     ap.add_argument("--path", choices=["fused", "staged"], default="fused",
                     help="fused: dispatch indices only, the gate/up GEMM gathers rows from x; "
                          "staged: dispatch gathers rows into x_perm first")
+    ap.add_argument("--graph", action="store_true",
+                    help="record one step in a HIP graph and time graph replays (the GEMM roofline "
+                         "then comes from an eager pass after the timed replays)")
     ap.add_argument("--clock-seconds", type=float, default=0.0,
                     help="after timing, repeat the step for this many seconds while sampling the "
                          "shader clock with rocm-smi; reports the median as sclk_mhz")
@@ -187,27 +190,29 @@ def main() -> int:
     h = torch.empty((w.n_max, w.d_ff), dtype=dx.dtype, device=dev)
     y = torch.empty((w.n_max, w.d), dtype=dx.dtype, device=dev)
     out = torch.empty((w.T, w.d), dtype=dx.dtype, device=dev)
-    stream = torch.cuda.current_stream()
+    # the stream every call goes to: torch's current stream at call time (the
+    # capture stream while a graph is being recorded)
+    cur = torch.cuda.current_stream
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
 
     def gemm():
         if fused:
             moe.grouped_gemm_gather(dx, disp.perm, disp.offsets, dgu, ddn, w.k, w.E, w.e_begin, w.e_end,
-                                    h=h, y=y, stream=stream)
+                                    h=h, y=y, stream=cur())
         else:
             moe.grouped_gemm(disp.x_perm, disp.offsets, dgu, ddn, w.T, w.k, w.E, w.e_begin, w.e_end,
-                             h=h, y=y, stream=stream)
+                             h=h, y=y, stream=cur())
 
     def step(i=None):
-        moe.route_topk(dl, w.k, idx, wts, stream=stream)
-        moe.dispatch(dx, idx, w.E, w.e_begin, w.e_end, out=disp, stream=stream, gather=not fused)
+        moe.route_topk(dl, w.k, idx, wts, stream=cur())
+        moe.dispatch(dx, idx, w.E, w.e_begin, w.e_end, out=disp, stream=cur(), gather=not fused)
         if i is not None:
-            ev[i][0].record(stream)
+            ev[i][0].record(cur())
         gemm()
         if i is not None:
-            ev[i][1].record(stream)
-        moe.combine(y, disp.pair_pos, wts, w.T, w.k, w.E, w.e_begin, w.e_end, out=out, stream=stream)
+            ev[i][1].record(cur())
+        moe.combine(y, disp.pair_pos, wts, w.T, w.k, w.E, w.e_begin, w.e_end, out=out, stream=cur())
 
     for _ in range(args.warmup):
         step()
@@ -216,13 +221,35 @@ def main() -> int:
     n_loc = int(offs[w.e_end] - offs[w.e_begin])
     active = int(np.count_nonzero(disp.counts.cpu().numpy()[w.e_begin:w.e_end]))
 
+    graph = None
+    if args.graph:
+        # one step recorded into a HIP graph (warmed up on a side stream first)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i)
+        if graph is not None:
+            graph.replay()
+        else:
+            step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
+    if graph is not None:  # the GEMM's events come from an eager pass after the timed replays
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
     gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
     flops = 6.0 * n_loc * w.d * w.d_ff  # gate/up (4 N d d_ff) + down (2 N d d_ff)
@@ -266,7 +293,8 @@ def main() -> int:
         "data": "synthetic (seeded normal draws; see moe_inputs)",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "d_ff": w.d_ff, "E": w.E, "k": w.k,
                    "local_experts": [w.e_begin, w.e_end], "N_loc": n_loc, "active_local_experts": active,
-                   "parallelism": "one rank's share on 1 GPU", "path": args.path},
+                   "parallelism": "one rank's share on 1 GPU", "path": args.path,
+                   "launch": "hip graph" if args.graph else "eager"},
         "local_pairs_per_s": round(n_loc / (ms_step * 1e-3), 1),
         "roofline": roofline,
         "cpu_baseline": None,
@@ -275,15 +303,15 @@ def main() -> int:
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     for i in range(args.steps):
         e = evs[i]
-        e[0].record(stream)
-        moe.route_topk(dl, w.k, idx, wts, stream=stream)
-        e[1].record(stream)
-        moe.dispatch(dx, idx, w.E, w.e_begin, w.e_end, out=disp, stream=stream, gather=not fused)
-        e[2].record(stream)
+        e[0].record(cur())
+        moe.route_topk(dl, w.k, idx, wts, stream=cur())
+        e[1].record(cur())
+        moe.dispatch(dx, idx, w.E, w.e_begin, w.e_end, out=disp, stream=cur(), gather=not fused)
+        e[2].record(cur())
         gemm()
-        e[3].record(stream)
-        moe.combine(y, disp.pair_pos, wts, w.T, w.k, w.E, w.e_begin, w.e_end, out=out, stream=stream)
-        e[4].record(stream)
+        e[3].record(cur())
+        moe.combine(y, disp.pair_pos, wts, w.T, w.k, w.E, w.e_begin, w.e_end, out=out, stream=cur())
+        e[4].record(cur())
     torch.cuda.synchronize()
     parts = ["route_topk", "dispatch", "grouped_gemm", "combine"]
     result["entry_point_ms"] = {p: round(float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])), 4)

@@ -1,0 +1,94 @@
+"""The whole layer captured in one HIP graph (the decode use the pages give for
+a path with no host synchronisation: "Paralelismo de especialistas", the
+masking variant that keeps shapes static).
+
+Every step of the layer takes its sizes from the host-side shape and its row
+counts from device memory, allocates nothing and never synchronises, so the
+four calls capture as they are. Each replay runs on new inputs copied into the
+captured buffers, with eager work and synchronisations between replays, and
+must equal the eager layer on the same inputs bit for bit.
+"""
+import numpy as np
+import pytest
+
+import moe_inputs as mi
+from tests import _gpu as g
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+import token_dispatch_grouped_amd as moe  # noqa: E402
+
+
+def _buffers(w, dev):
+    T, k = w.T, w.k
+    n_max = T * min(k, w.E_loc)
+    x = torch.empty((T, w.d), dtype=torch.bfloat16, device=dev)
+    logits = torch.empty((T, w.E), dtype=torch.float32, device=dev)
+    return dict(
+        x=x, logits=logits,
+        idx=torch.empty((T, k), dtype=torch.int32, device=dev),
+        w=torch.empty((T, k), dtype=torch.float32, device=dev),
+        h=torch.empty((n_max, w.d_ff), dtype=torch.bfloat16, device=dev),
+        y=torch.empty((n_max, w.d), dtype=torch.bfloat16, device=dev),
+        out=torch.empty((T, w.d), dtype=torch.bfloat16, device=dev),
+    )
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "staged"])
+def test_layer_graph_replays_match_eager(fused):
+    w = mi.Workload("graph_decode", 48, 256, 192, 64, 4, 0, 64, "bf16", 31)
+    dev = torch.device("cuda:0")
+    wgu, wdn = mi.expert_weights(w)
+    dgu, ddn = g.to_dev(wgu, "bf16"), g.to_dev(wdn, "bf16")
+    b = _buffers(w, dev)
+    disp = moe.dispatch_alloc(b["x"], w.k, w.E, w.e_begin, w.e_end, gather=not fused)
+
+    def step():
+        moe.route_topk(b["logits"], w.k, b["idx"], b["w"])
+        moe.dispatch(b["x"], b["idx"], w.E, w.e_begin, w.e_end, out=disp, gather=not fused)
+        if fused:
+            moe.grouped_gemm_gather(b["x"], disp.perm, disp.offsets, dgu, ddn, w.k, w.E, w.e_begin, w.e_end,
+                                    h=b["h"], y=b["y"])
+        else:
+            moe.grouped_gemm(disp.x_perm, disp.offsets, dgu, ddn, w.T, w.k, w.E, w.e_begin, w.e_end,
+                             h=b["h"], y=b["y"])
+        moe.combine(b["y"], disp.pair_pos, b["w"], w.T, w.k, w.E, w.e_begin, w.e_end, out=b["out"])
+
+    def load_inputs(seed):
+        rng = np.random.default_rng(seed)
+        x = mi.f32_to_bf16_bits(rng.standard_normal((w.T, w.d)).astype(np.float32))
+        lg = rng.standard_normal((w.T, w.E)).astype(np.float32)
+        b["x"].copy_(g.to_dev(x, "bf16"))
+        b["logits"].copy_(g.to_dev(lg, "f32"))
+        return x, lg
+
+    load_inputs(0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+
+    for seed in (1, 2, 3, 4):
+        x, lg = load_inputs(seed)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = b["out"].clone()
+        got_idx = b["idx"].clone()
+        # the eager layer on the same inputs, in separate buffers
+        eager = moe.layer(g.to_dev(x, "bf16"), g.to_dev(lg, "f32"), dgu, ddn, w.k, w.e_begin, w.e_end,
+                          fused=fused)
+        torch.cuda.synchronize()
+        assert torch.equal(got_idx, eager["idx"]), seed
+        assert torch.equal(got, eager["out"]), seed
+        assert torch.count_nonzero(got).item() > 0
