@@ -1,4 +1,4 @@
-"""CPU oracle of the MoE expert-layer forward — TEST INFRASTRUCTURE ONLY.
+"""CPU oracle of the MoE expert-layer forward and its gradient — TEST INFRASTRUCTURE ONLY.
 
 Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
 this package. The GPU path never calls it and shares no code with it.
@@ -15,4 +15,13 @@ from .moe import (  # noqa: F401
     moe_layer,
     brute_force_dense,
     token_outputs,
+)
+from .moe_backward import (  # noqa: F401
+    silu_grad,
+    route_topk_backward,
+    combine_backward,
+    swiglu_backward,
+    expert_ffn_backward,
+    dispatch_backward,
+    moe_layer_backward,
 )
