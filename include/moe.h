@@ -182,6 +182,72 @@ moe_status moe_combine(const moe_shape* s, moe_dtype dt, const void* y,
                        const int32_t* pair_pos, const float* topk_w, void* out,
                        hipStream_t stream);
 
+/* ------------------------------------------------------------------ backward
+ * The gradient of the forward above, step by step in reverse order. The pages
+ * ask for it as the training use of the layer ("Paralelismo de especialistas":
+ * gradients return to every rank that holds a token; the masking variant's
+ * partial outputs are summed across ranks, so are their gradients) and give no
+ * formula: each call is the chain rule through the forward call of the same
+ * name. On one rank every gradient is that rank's partial gradient; their sum
+ * over ranks is the full one. Gradients arrive and leave in dt (d_topk_w and
+ * d_logits in fp32) and accumulate in fp32. */
+
+/* Gradient of moe_combine:
+ *     d_y[r]        = topk_w[t, j] * d_out[t]    for the local pair (t, j) at row r
+ *     d_topk_w[t, j] = <d_out[t], y[r]>           (0 when pair (t, j) is not local)
+ *   d_out    [T, d] dt, read only: gradient of the layer output.
+ *   y, pair_pos, topk_w: as passed to moe_combine.
+ *   d_y      [N_max, d] dt, written: rows [0, N_loc).
+ *   d_topk_w [T, k] fp32, written. */
+moe_status moe_combine_backward(const moe_shape* s, moe_dtype dt, const void* d_out,
+                                const void* y, const int32_t* pair_pos, const float* topk_w,
+                                void* d_y, float* d_topk_w, hipStream_t stream);
+
+/* Bytes of device workspace moe_grouped_gemm_backward needs (0 unless dt is
+ * MOE_BF16): the gathered rows, and the gate/up pre-activations and their
+ * gradient, each for N_max rows. */
+size_t moe_grouped_gemm_backward_workspace_bytes(const moe_shape* s, moe_dtype dt);
+
+/* Gradient of the grouped expert FFN (moe_grouped_gemm / _gather). For each local
+ * expert e with rows R, [G | U] = X_R @ W_gu[e] (recomputed here), H = silu(G) * U:
+ *     dH = d_y @ W_dn[e]^T;  dG = dH * U * silu'(G);  dU = dH * silu(G)
+ *     d_x_perm = [dG | dU] @ W_gu[e]^T
+ *     d_w_down[e]    = H^T @ d_y
+ *     d_w_gate_up[e] = X_R^T @ [dG | dU]
+ *   x, perm   the hidden states [T, d] and the dispatch's perm (as for
+ *             moe_grouped_gemm_gather; X_R are the gathered rows).
+ *   offsets, w_gate_up, w_down: as for the forward.
+ *   h         [N_max, d_ff] dt, read only: the forward's h.
+ *   d_y       [N_max, d] dt, read only: from moe_combine_backward.
+ *   d_x_perm  [N_max, d] dt, written: rows [0, N_loc).
+ *   d_w_gate_up [E_loc, d, 2*d_ff] dt, d_w_down [E_loc, d_ff, d] dt, written in
+ *             full (zero for an expert with no rows).
+ *   workspace moe_grouped_gemm_backward_workspace_bytes(s, dt) bytes.
+ * MOE_EUNSUPPORTED unless dt = MOE_BF16, d and d_ff are multiples of 32, and the
+ * activation blocks (N_max rows of max(d, 2*d_ff)) and x fit 31-bit byte offsets. */
+moe_status moe_grouped_gemm_backward(const moe_shape* s, moe_dtype dt, const void* x,
+                                     const int32_t* perm, const int32_t* offsets,
+                                     const void* w_gate_up, const void* w_down, const void* h,
+                                     const void* d_y, void* d_x_perm, void* d_w_gate_up,
+                                     void* d_w_down, void* workspace, hipStream_t stream);
+
+/* Gradient of the dispatch's row gather: d_x[t] = sum over t's local pairs (slot
+ * order, fp32) of d_x_perm[pair_pos[t*k + j]]; zero rows for tokens without one.
+ *   d_x_perm [N_max, d] dt, read only.  pair_pos: as from moe_dispatch.
+ *   d_x      [T, d] dt, written (every row). */
+moe_status moe_dispatch_backward(const moe_shape* s, moe_dtype dt, const void* d_x_perm,
+                                 const int32_t* pair_pos, void* d_x, hipStream_t stream);
+
+/* Gradient of the combine weights of moe_route_topk w.r.t. the logits (softmax
+ * over the selected logits; the selection passes no gradient):
+ *     d_logits[t, topk_idx[t, j]] = topk_w[t, j] * (d_topk_w[t, j] - sum_i topk_w[t, i] * d_topk_w[t, i])
+ * and 0 for every other expert.
+ *   topk_idx, topk_w [T, k]: from moe_route_topk (ids of a token distinct).
+ *   d_topk_w [T, k] fp32, read only.   d_logits [T, E] fp32, written (every entry). */
+moe_status moe_route_topk_backward(const moe_shape* s, const int32_t* topk_idx,
+                                   const float* topk_w, const float* d_topk_w, float* d_logits,
+                                   hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

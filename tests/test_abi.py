@@ -157,3 +157,38 @@ def test_fused_path_entry_points_validate_on_the_host():
     assert _gemm_gather(_shape(T=2**20, d=1024, k=1)) == moe.MOE_EUNSUPPORTED
     # T = 0: nothing is enqueued
     assert _gemm_gather(_shape(T=0), ptrs=[NULL] * 7) == moe.MOE_OK
+
+
+def test_backward_entry_points_validate_on_the_host():
+    lib = moe.lib()
+    s = _shape()
+    # combine backward: 6 pointers
+    for i in range(6):
+        p = [FAKE] * 6
+        p[i] = NULL
+        assert lib.moe_combine_backward(ctypes.byref(s), moe.MOE_BF16, *p, NULL) == moe.MOE_EINVAL, i
+    # grouped GEMM backward: 10 pointers before the workspace
+    for i in range(10):
+        p = [FAKE] * 10
+        p[i] = NULL
+        assert lib.moe_grouped_gemm_backward(ctypes.byref(s), moe.MOE_BF16, *p, FAKE, NULL) == moe.MOE_EINVAL, i
+    assert lib.moe_grouped_gemm_backward(ctypes.byref(s), moe.MOE_BF16, *([FAKE] * 10), NULL, NULL) == moe.MOE_EINVAL
+    assert lib.moe_grouped_gemm_backward(ctypes.byref(s), moe.MOE_F32, *([FAKE] * 11), NULL) == moe.MOE_EUNSUPPORTED
+    s72 = _shape(d=72)
+    assert lib.moe_grouped_gemm_backward(ctypes.byref(s72), moe.MOE_BF16, *([FAKE] * 11), NULL) == \
+        moe.MOE_EUNSUPPORTED
+    # dispatch and route backward
+    for i in range(3):
+        p = [FAKE] * 3
+        p[i] = NULL
+        assert lib.moe_dispatch_backward(ctypes.byref(s), moe.MOE_BF16, *p, NULL) == moe.MOE_EINVAL, i
+    for i in range(4):
+        p = [FAKE] * 4
+        p[i] = NULL
+        assert lib.moe_route_topk_backward(ctypes.byref(s), *p, NULL) == moe.MOE_EINVAL, i
+    # workspace: x_perm [N_max, d] and two [N_max, 2 d_ff] blocks, each 256-byte aligned; none for fp32
+    s = _shape(T=16, d=64, d_ff=64, k=2)
+    n_max = 32
+    assert lib.moe_grouped_gemm_backward_workspace_bytes(ctypes.byref(s), moe.MOE_BF16) == \
+        n_max * 64 * 2 + 2 * n_max * 128 * 2
+    assert lib.moe_grouped_gemm_backward_workspace_bytes(ctypes.byref(s), moe.MOE_F32) == 0

@@ -1,0 +1,137 @@
+"""GPU parity of the backward path against the fp64 backward oracle.
+
+moe.layer (fused forward) then moe.layer_backward on a seeded d_out; every
+gradient is compared with oracle.moe_layer_backward on the same bf16 inputs:
+max|err| / max|ref| within the bf16 tolerance (the GPU rounds y, h, the
+recomputed gate/up pre-activations and the intermediate gradients to bf16; the
+oracle rounds nothing).
+"""
+import numpy as np
+import pytest
+
+import moe_inputs as mi
+import oracle
+from tests import _gpu as g
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+import token_dispatch_grouped_amd as moe  # noqa: E402
+
+TOL = g.TOL["bf16"]
+
+
+def _d_out(w):
+    rng = np.random.default_rng(w.seed + 500)
+    return mi.f32_to_bf16_bits(rng.standard_normal((w.T, w.d)).astype(np.float32))
+
+
+def _backward_case(w, logits=None):
+    if logits is None:
+        logits = mi.router_logits(w)
+    x = mi.hidden_states(w)
+    wgu, wdn = mi.expert_weights(w)
+    d_out = _d_out(w)
+    print(f"case {w}", flush=True)
+    dx, dl = g.to_dev(x, "bf16"), g.to_dev(logits, "f32")
+    dgu, ddn = g.to_dev(wgu, "bf16"), g.to_dev(wdn, "bf16")
+    fwd = moe.layer(dx, dl, dgu, ddn, w.k, w.e_begin, w.e_end, fused=True)
+    bwd = moe.layer_backward(dx, dgu, ddn, fwd, g.to_dev(d_out, "bf16"), w.k, w.e_begin, w.e_end)
+    torch.cuda.synchronize()
+    x64, wgu64, wdn64 = mi.to_f64(x, "bf16"), mi.to_f64(wgu, "bf16"), mi.to_f64(wdn, "bf16")
+    ref = oracle.moe_layer_backward(x64, logits, w.k, w.e_begin, w.e_end, list(wgu64), list(wdn64),
+                                    mi.to_f64(d_out, "bf16"))
+    n_loc = ref["x_perm"].shape[0]
+    errs = {}
+    if n_loc:
+        errs["d_y"] = g.rel_err(g.to_f64(bwd["d_y"][:n_loc]), ref["d_y"])
+        errs["d_x_perm"] = g.rel_err(g.to_f64(bwd["d_x_perm"][:n_loc]), ref["d_x_perm"])
+        errs["d_w"] = g.rel_err(bwd["d_w"].cpu().numpy().astype(np.float64), ref["d_w"])
+        errs["d_logits"] = g.rel_err(bwd["d_logits"].cpu().numpy().astype(np.float64), ref["d_logits"])
+        errs["d_x"] = g.rel_err(g.to_f64(bwd["d_x"]), ref["d_x"])
+    for name in ("d_w_gate_up", "d_w_down"):
+        got = g.to_f64(bwd[name])
+        if np.any(ref[name]):
+            errs[name] = g.rel_err(got, ref[name])
+        else:
+            assert np.all(got == 0), name
+    print("  " + ", ".join(f"{k_}={v:.2e}" for k_, v in errs.items()), flush=True)
+    for name, err in errs.items():
+        assert err <= TOL, (name, err)
+    # gradients of pairs that are not local are exactly zero
+    pp = ref["pair_pos"].reshape(w.T, w.k)
+    assert np.all(bwd["d_w"].cpu().numpy()[pp < 0] == 0)
+    no_local = ~(pp >= 0).any(axis=1)
+    assert np.all(g.to_f64(bwd["d_x"])[no_local] == 0)
+    # experts without rows get zero weight gradients
+    counts = np.diff(ref["offsets"])[w.e_begin:w.e_end]
+    for el in np.flatnonzero(counts == 0):
+        assert torch.count_nonzero(bwd["d_w_gate_up"][el]).item() == 0
+        assert torch.count_nonzero(bwd["d_w_down"][el]).item() == 0
+    return fwd, bwd, ref
+
+
+CASES = [
+    mi.Workload("bwd_small", 600, 256, 160, 8, 2, 0, 8, "bf16", 41),
+    mi.Workload("bwd_share", 900, 192, 128, 32, 4, 8, 16, "bf16", 42),
+    mi.Workload("bwd_skew", 1000, 320, 128, 64, 8, 0, 16, "bf16", 43, 1.5),   # skewed, empty experts
+    mi.Workload("bwd_decode", 5, 256, 192, 128, 4, 0, 128, "bf16", 44),       # mostly empty experts
+    mi.Workload("bwd_ragged_dims", 700, 288, 96, 8, 2, 0, 8, "bf16", 45),    # d, d_ff not multiples of 256
+]
+
+
+@pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
+def test_layer_backward_matches_oracle(w):
+    _backward_case(w)
+
+
+def _one_hot_logits(counts, E, seed):
+    rng = np.random.default_rng(seed)
+    T = int(sum(counts))
+    owner = np.repeat(np.arange(E), counts)
+    rng.shuffle(owner)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[np.arange(T), owner] += 50.0
+    return logits
+
+
+def test_backward_every_row_count():
+    """Expert row counts at the edges of the row tiles (forward and NT) and of the
+    32-row K stages of the weight gradients, including empty experts."""
+    counts = [0, 1, 31, 32, 33, 63, 64, 65, 255, 256, 257, 300, 0, 513]
+    E = len(counts)
+    w = mi.Workload("bwd_rows", int(sum(counts)), 256, 160, E, 1, 0, E, "bf16", 46)
+    _backward_case(w, _one_hot_logits(counts, E, 46))
+
+
+def test_backward_zero_tokens_writes_zero_weight_gradients():
+    w = mi.Workload("bwd_empty", 0, 64, 64, 8, 2, 0, 8, "bf16", 47)
+    wgu, wdn = mi.expert_weights(w)
+    dgu, ddn = g.to_dev(wgu, "bf16"), g.to_dev(wdn, "bf16")
+    offsets = torch.zeros(w.E + 1, dtype=torch.int32, device="cuda")
+    x = torch.empty((0, w.d), dtype=torch.bfloat16, device="cuda")
+    perm = torch.empty(0, dtype=torch.int32, device="cuda")
+    h = torch.empty((0, w.d_ff), dtype=torch.bfloat16, device="cuda")
+    d_y = torch.empty((0, w.d), dtype=torch.bfloat16, device="cuda")
+    d_wgu = torch.full_like(dgu, 3.0)
+    d_wdn = torch.full_like(ddn, 3.0)
+    moe.grouped_gemm_backward(x, perm, offsets, dgu, ddn, h, d_y, w.k, w.E, w.e_begin, w.e_end,
+                              d_w_gate_up=d_wgu, d_w_down=d_wdn)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(d_wgu).item() == 0 and torch.count_nonzero(d_wdn).item() == 0
+
+
+def test_backward_rejects_unsupported_shapes():
+    x = torch.zeros((16, 72), dtype=torch.bfloat16, device="cuda")  # d not a multiple of 32
+    perm = torch.zeros(32, dtype=torch.int32, device="cuda")
+    offsets = torch.zeros(9, dtype=torch.int32, device="cuda")
+    wgu = torch.zeros((8, 72, 128), dtype=torch.bfloat16, device="cuda")
+    wdn = torch.zeros((8, 64, 72), dtype=torch.bfloat16, device="cuda")
+    h = torch.zeros((32, 64), dtype=torch.bfloat16, device="cuda")
+    d_y = torch.zeros((32, 72), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(moe.MoeError) as e:
+        moe.grouped_gemm_backward(x, perm, offsets, wgu, wdn, h, d_y, 2, 8, 0, 8)
+    assert e.value.status == moe.MOE_EUNSUPPORTED

@@ -63,6 +63,11 @@ def _load():
             "moe_grouped_gemm_workspace_bytes": (SZ, [S, ctypes.c_int]),
             "moe_grouped_gemm": (ctypes.c_int, [S, ctypes.c_int, P, P, P, P, P, P, P, P]),
             "moe_combine": (ctypes.c_int, [S, ctypes.c_int, P, P, P, P, P]),
+            "moe_combine_backward": (ctypes.c_int, [S, ctypes.c_int, P, P, P, P, P, P, P]),
+            "moe_grouped_gemm_backward_workspace_bytes": (SZ, [S, ctypes.c_int]),
+            "moe_grouped_gemm_backward": (ctypes.c_int, [S, ctypes.c_int, P, P, P, P, P, P, P, P, P, P, P, P]),
+            "moe_dispatch_backward": (ctypes.c_int, [S, ctypes.c_int, P, P, P, P]),
+            "moe_route_topk_backward": (ctypes.c_int, [S, P, P, P, P, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(lib, name)
@@ -299,3 +304,85 @@ def layer(x, logits, w_gate_up, w_down, k: int, e_begin: int, e_end: int, stream
     out = combine(y, disp.pair_pos, w, T, k, E, e_begin, e_end, stream=stream)
     return dict(idx=idx, w=w, counts=disp.counts, offsets=disp.offsets, perm=disp.perm,
                 pair_pos=disp.pair_pos, x_perm=disp.x_perm, h=h, y=y, out=out)
+
+
+# ----------------------------------------------------------------------------- backward
+
+def combine_backward(d_out, y, pair_pos, topk_w, T: int, k: int, E: int, e_begin: int, e_end: int,
+                     d_y=None, d_topk_w=None, stream=None):
+    """(d_y [N_max, d], d_topk_w [T, k] fp32): the gradient of combine."""
+    torch = _torch()
+    _dev(d_out, y, pair_pos, topk_w)
+    d = d_out.shape[1]
+    if d_y is None:
+        d_y = torch.empty_like(y)
+    if d_topk_w is None:
+        d_topk_w = torch.empty((T, k), dtype=torch.float32, device=d_out.device)
+    s = shape(T, d, 8, E, k, e_begin, e_end)
+    _check(_load().moe_combine_backward(ctypes.byref(s), _dtype_code(d_out), _ptr(d_out), _ptr(y), _ptr(pair_pos),
+                                        _ptr(topk_w), _ptr(d_y), _ptr(d_topk_w), _stream(stream)),
+           "moe_combine_backward")
+    return d_y, d_topk_w
+
+
+def grouped_gemm_backward(x, perm, offsets, w_gate_up, w_down, h, d_y, k: int, E: int, e_begin: int, e_end: int,
+                          d_x_perm=None, d_w_gate_up=None, d_w_down=None, stream=None):
+    """(d_x_perm, d_w_gate_up, d_w_down): the gradient of the grouped expert FFN."""
+    torch = _torch()
+    _dev(x, perm, offsets, w_gate_up, w_down, h, d_y)
+    T, d = x.shape
+    e_loc, d_ff, _ = w_down.shape
+    s = shape(T, d, d_ff, E, k, e_begin, e_end)
+    dt = _dtype_code(x)
+    if d_x_perm is None:
+        d_x_perm = torch.empty_like(d_y)
+    if d_w_gate_up is None:
+        d_w_gate_up = torch.empty_like(w_gate_up)
+    if d_w_down is None:
+        d_w_down = torch.empty_like(w_down)
+    ws_bytes = _load().moe_grouped_gemm_backward_workspace_bytes(ctypes.byref(s), dt)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device) if ws_bytes else None
+    _check(_load().moe_grouped_gemm_backward(ctypes.byref(s), dt, _ptr(x), _ptr(perm), _ptr(offsets),
+                                             _ptr(w_gate_up), _ptr(w_down), _ptr(h), _ptr(d_y), _ptr(d_x_perm),
+                                             _ptr(d_w_gate_up), _ptr(d_w_down), _ptr(ws), _stream(stream)),
+           "moe_grouped_gemm_backward")
+    return d_x_perm, d_w_gate_up, d_w_down
+
+
+def dispatch_backward(d_x_perm, pair_pos, T: int, k: int, E: int, e_begin: int, e_end: int, d_x=None, stream=None):
+    """d_x [T, d]: the gradient of the row gather."""
+    torch = _torch()
+    _dev(d_x_perm, pair_pos)
+    d = d_x_perm.shape[1]
+    if d_x is None:
+        d_x = torch.empty((T, d), dtype=d_x_perm.dtype, device=d_x_perm.device)
+    s = shape(T, d, 8, E, k, e_begin, e_end)
+    _check(_load().moe_dispatch_backward(ctypes.byref(s), _dtype_code(d_x_perm), _ptr(d_x_perm), _ptr(pair_pos),
+                                         _ptr(d_x), _stream(stream)), "moe_dispatch_backward")
+    return d_x
+
+
+def route_topk_backward(topk_idx, topk_w, d_topk_w, E: int, d_logits=None, stream=None):
+    """d_logits [T, E] fp32: the gradient of route_topk's weights w.r.t. the logits."""
+    torch = _torch()
+    _dev(topk_idx, topk_w, d_topk_w)
+    T, k = topk_idx.shape
+    if d_logits is None:
+        d_logits = torch.empty((T, E), dtype=torch.float32, device=topk_idx.device)
+    s = shape(T, 8, 8, E, k, 0, E)
+    _check(_load().moe_route_topk_backward(ctypes.byref(s), _ptr(topk_idx), _ptr(topk_w), _ptr(d_topk_w),
+                                           _ptr(d_logits), _stream(stream)), "moe_route_topk_backward")
+    return d_logits
+
+
+def layer_backward(x, w_gate_up, w_down, fwd: dict, d_out, k: int, e_begin: int, e_end: int, stream=None) -> dict:
+    """The whole backward of one rank, given the forward's dict (from layer()):
+    combine -> experts -> row gather -> router softmax."""
+    T = x.shape[0]
+    E = fwd["counts"].shape[0]
+    d_y, d_w = combine_backward(d_out, fwd["y"], fwd["pair_pos"], fwd["w"], T, k, E, e_begin, e_end, stream=stream)
+    d_x_perm, d_wgu, d_wdn = grouped_gemm_backward(x, fwd["perm"], fwd["offsets"], w_gate_up, w_down, fwd["h"], d_y,
+                                                   k, E, e_begin, e_end, stream=stream)
+    d_x = dispatch_backward(d_x_perm, fwd["pair_pos"], T, k, E, e_begin, e_end, stream=stream)
+    d_logits = route_topk_backward(fwd["idx"], fwd["w"], d_w, E, stream=stream)
+    return dict(d_y=d_y, d_w=d_w, d_x_perm=d_x_perm, d_w_gate_up=d_wgu, d_w_down=d_wdn, d_x=d_x, d_logits=d_logits)

@@ -60,7 +60,7 @@ struct Vec<false> {  // 4 fp32 per 16 bytes
   }
 };
 
-template <bool BF16>
+template <bool BF16, bool UNIT>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const uint4* __restrict__ y,
                                                            const int32_t* __restrict__ pair_pos,
                                                            const float* __restrict__ w,
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint4* __restri
       for (int j0 = 0; j0 < k; j0 += kWave) {
         const int j = j0 + lane;
         const int rl = j < k ? pair_pos[pbase + j] : -1;
-        const float wl = j < k ? w[pbase + j] : 0.f;
+        const float wl = UNIT ? 1.f : (j < k ? w[pbase + j] : 0.f);
         uint64_t mask = __ballot(rl >= 0 && rl < n_max);
         // local slots two at a time, both rows' loads in flight together, added in slot order
         while (mask) {
@@ -158,15 +158,18 @@ hipError_t launch_combine(const void* y, const int32_t* pair_pos, const float* w
   const int row_vec = bf16 ? d / 8 : d / 4;
   int64_t blocks = (T + (kThreads / kWave) - 1) / (kThreads / kWave);
   if (blocks > 4096) blocks = 4096;
+#define MOE_COMBINE_LAUNCH(B, U)                                                                         \
+  hipLaunchKernelGGL((combine_kernel<B, U>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, \
+                     static_cast<const uint4*>(y), pair_pos, w, static_cast<uint4*>(out), T, k, row_vec, n_max)
+  // w == nullptr: every local pair has weight 1 (the gradient of the row gather)
   if (bf16) {
-    hipLaunchKernelGGL(combine_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                       stream, static_cast<const uint4*>(y), pair_pos, w, static_cast<uint4*>(out), T,
-                       k, row_vec, n_max);
+    if (w) MOE_COMBINE_LAUNCH(true, false);
+    else MOE_COMBINE_LAUNCH(true, true);
   } else {
-    hipLaunchKernelGGL(combine_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                       stream, static_cast<const uint4*>(y), pair_pos, w, static_cast<uint4*>(out), T,
-                       k, row_vec, n_max);
+    if (w) MOE_COMBINE_LAUNCH(false, false);
+    else MOE_COMBINE_LAUNCH(false, true);
   }
+#undef MOE_COMBINE_LAUNCH
   return hipGetLastError();
 }
 

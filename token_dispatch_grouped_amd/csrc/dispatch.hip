@@ -261,6 +261,11 @@ hipError_t launch_dispatch(const void* x, size_t row_bytes, const int32_t* idx, 
   hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(n_chunks), dim3(kThreads), 0, stream, idx, bases,
                      offsets, perm, pair_pos, P, E, e_begin, e_end);
   if (x_perm == nullptr) return hipGetLastError();  // indices only: the rows are gathered by the GEMM
+  return launch_gather_rows(x, row_bytes, perm, offsets, x_perm, k, e_begin, e_end, n_max, stream);
+}
+
+hipError_t launch_gather_rows(const void* x, size_t row_bytes, const int32_t* perm, const int32_t* offsets,
+                              void* x_perm, int k, int e_begin, int e_end, int64_t n_max, hipStream_t stream) {
   const int row_vec = static_cast<int>(row_bytes / 16);
   const int parts = (row_vec + kGatherVec - 1) / kGatherVec;
   const int64_t waves_needed = n_max * parts;  // one wave per row part at most

@@ -304,6 +304,10 @@ int grid_for(int64_t n_max, int e_loc, int bm, int n_tiles, int per_cu) {
 
 }  // namespace
 
+int grouped_gemm_grid(int64_t n_max, int e_loc, int n_tiles) { return grid_for(n_max, e_loc, kBM, n_tiles, 1); }
+
+int device_cu_count() { return device_cus(); }
+
 hipError_t launch_grouped_gemm_bf16(const void* x_perm, const int32_t* offsets, const void* w_gu,
                                     const void* w_dn, void* h, void* y, int d, int d_ff, int e_begin,
                                     int e_loc, int64_t n_max, int64_t T, int k, int E,

@@ -1,0 +1,411 @@
+// Backward of the grouped expert FFN: the four products of its gradient.
+//
+// What is computed is the chain rule through experts_forward of "Paralelismo de
+// especialistas" (transformers v5.23.0, pt), section "Adicionando uma
+// implementação", with the packed gate_up_proj of "Paralelismo de tensor para
+// inferência", section "Estratégias empacotadas", and SwiGLU = silu(gate) * up.
+// For each local expert e with rows R (its segment of the dispatched rows):
+//     dH    = dY @ W_dn[e]^T, then dG = dH * U * silu'(G), dU = dH * silu(G)
+//     dX    = [dG | dU] @ W_gu[e]^T
+//     dW_dn = H^T @ dY
+//     dW_gu = X^T @ [dG | dU]
+// with fp32 accumulation and bf16 (RNE) results.
+//
+// Two tile kinds share the forward kernel's pipeline (LDS-DMA stages of K = 32,
+// four stages, reads and loads issued one per MFMA slot):
+//   * NT (dH, dX): row tiles of an expert's rows as in the forward; both operands
+//     are K-contiguous rows (the activations, and the weights read along their
+//     contiguous dimension, which is the product's K here), so both are staged
+//     as [row][32] and read with ds_read_b128.
+//   * TN (dW): a tile is 256 x 256 of one expert's weight gradient and K runs
+//     over the expert's rows (any count, zero included); both operands are
+//     row-major activations with M or N contiguous, so both are staged as
+//     [k][256] and read back transposed with ds_read_b64_tr_b16.
+// Waves: 2 x 2, each 128 x 128 (4 x 4 MFMA blocks of 32 x 32).
+#include "lds_pipe.h"
+
+namespace moe {
+namespace {
+
+using namespace gemm;
+
+constexpr int kBK = 32;
+constexpr int kStages = 4;
+constexpr int kOpStageBytes = 256 * kBK * 2;  // 16 KB per operand per stage
+constexpr int MI = 4, NI = 4, PER = 8;        // blocks per wave; DMA loads per wave per stage
+
+enum Mode { kNT = 0, kTN = 1 };
+enum Epi { kPlain = 0, kSwigluBwd = 1 };
+
+template <int MODE>
+struct Frags;
+template <>
+struct Frags<kNT> {
+  bf16x8_t a[MI], b[NI];
+};
+template <>
+struct Frags<kTN> {
+  i16x4_t a[MI][2], b[NI][2];
+};
+
+// One operand of a tile as the DMA and the fragment reads see it.
+struct Operand {
+  const uint16_t* base;  // first element of the tile's rows (KROWS) or k-rows (KMAJOR) at stage 0
+  uint32_t bytes;        // bytes from base that are valid (past them: zeros)
+  uint32_t stage_step;   // bytes base advances per stage
+  uint32_t voff[4];      // per-lane byte offsets of this wave's 4 loads
+};
+
+// KROWS operand ([row][K], K contiguous): load j of a stage covers rows
+// 16j..16j+15, lane L row 16j + L/4, 16-byte chunk (L & 3) ^ ((row >> 2) & 3).
+__device__ __forceinline__ Operand krows_operand(const uint16_t* rows, int valid_rows, int ld, int wave, int lane) {
+  Operand op;
+  op.base = rows;
+  op.bytes = static_cast<uint32_t>(valid_rows) * static_cast<uint32_t>(ld) * 2u;
+  op.stage_step = kBK * 2;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int j = wave * 4 + jj;
+    const int r = 16 * j + (lane >> 2);
+    const int c = (lane & 3) ^ ((lane >> 4) & 3);
+    op.voff[jj] = static_cast<uint32_t>(r) * static_cast<uint32_t>(ld) * 2u + static_cast<uint32_t>(c) * 16u;
+  }
+  return op;
+}
+
+// KMAJOR operand ([k][ld], the tile's 256 columns from col0): load j of a stage
+// covers k-rows 2j, 2j+1, lane L k-row 2j + L/32, chunk (L & 31) ^ (4 * (k & 3)).
+__device__ __forceinline__ Operand kmajor_operand(const uint16_t* krows, int valid_krows, int ld, int col0, int wave,
+                                                  int lane) {
+  Operand op;
+  op.base = krows;
+  op.bytes = static_cast<uint32_t>(valid_krows) * static_cast<uint32_t>(ld) * 2u;
+  op.stage_step = static_cast<uint32_t>(kBK) * static_cast<uint32_t>(ld) * 2u;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int j = wave * 4 + jj;
+    const int kl = 2 * j + (lane >> 5);
+    const int c = (lane & 31) ^ (4 * (kl & 3));
+    op.voff[jj] = (static_cast<uint32_t>(kl) * static_cast<uint32_t>(ld) + static_cast<uint32_t>(col0 + 8 * c)) * 2u;
+  }
+  return op;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t stage_rsrc(const Operand& op, int s) {
+  const uint32_t adv = static_cast<uint32_t>(s) * op.stage_step;
+  return make_rsrc(reinterpret_cast<const char*>(op.base) + adv, op.bytes > adv ? op.bytes - adv : 0u);
+}
+
+// Byte offset, inside a KROWS stage, of block-row base `rb` (a multiple of 32)
+// for slice kk: lane reads row rb + l31, logical chunk 2 kk + lane / 32.
+__device__ __forceinline__ uint32_t krows_read(int rb, int kk, int lane) {
+  const int l31 = lane & 31;
+  const int c = (2 * kk + (lane >> 5)) ^ ((l31 >> 2) & 3);
+  return static_cast<uint32_t>((rb + l31) * kBK + c * 8) * 2u;
+}
+
+// Byte offset, inside a KMAJOR stage, of column block `cb`: two transposed reads
+// (imm 0 and 2048, plus 8192 for slice 1) give lane l column cb + l % 32, k 8(l/32)..+7.
+__device__ __forceinline__ uint32_t kmajor_read(int cb, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const int kl = (g >> 1) * 8 + (i >> 2);
+  const int n = cb + (g & 1) * 16 + 4 * (i & 3);
+  return static_cast<uint32_t>(kl * 256 + (((n >> 3) ^ (4 * (kl & 3))) * 8) + (n & 4)) * 2u;
+}
+
+__device__ __forceinline__ float sigmoid_fast(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+
+// up_off (kSwigluBwd): columns between gate and up halves of C and gu (= N).
+template <int MODE, int EPI>
+__device__ __forceinline__ void bwd_tile(uint16_t* smem, const Operand& opa, const Operand& opb, int ksteps,
+                                         uint16_t* __restrict__ C, int c_rows, int c_cols, int ldc,
+                                         const uint16_t* __restrict__ gu, int up_off) {
+  const int lane = lane_id();
+  const int wave = uniform(static_cast<int>(threadIdx.x) / kWave);
+  const int wm = wave / 2, wn = wave % 2;
+  const int l31 = lane & 31;
+  const uint32_t sA = uniform(static_cast<int>(lds_addr(smem)));
+  const uint32_t sB = sA + kStages * kOpStageBytes;
+
+  // fragment read offsets
+  uint32_t a_rd[2], b_rd[2], at_rd[MI], bt_rd[NI];
+  if constexpr (MODE == kNT) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      a_rd[kk] = krows_read(wm * 128, kk, lane);
+      b_rd[kk] = krows_read(wn * 128, kk, lane);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) at_rd[i] = kmajor_read(wm * 128 + i * 32, lane);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) bt_rd[i] = kmajor_read(wn * 128 + i * 32, lane);
+  }
+  // LDS reads of one 16-wide K slice: r < 4 the A blocks, then the B blocks (KROWS:
+  // one ds_read_b128 each; KMAJOR: two transposed reads each)
+  constexpr int R = MODE == kNT ? MI + NI : 2 * (MI + NI);
+  auto read_one = [&](Frags<MODE>& f, int buf, auto kk_c, auto r_c) {
+    constexpr int kk = decltype(kk_c)::value, r = decltype(r_c)::value;
+    if constexpr (MODE == kNT) {
+      if constexpr (r < MI) f.a[r] = ds_read16<r * 2048>(sA + buf * kOpStageBytes + a_rd[kk]);
+      else f.b[r - MI] = ds_read16<(r - MI) * 2048>(sB + buf * kOpStageBytes + b_rd[kk]);
+    } else {
+      constexpr int blk = (r % (2 * MI)) / 2, h = r % 2;
+      if constexpr (r < 2 * MI) f.a[blk][h] = ds_read_tr<kk * 8192 + h * 2048>(sA + buf * kOpStageBytes + at_rd[blk]);
+      else f.b[blk][h] = ds_read_tr<kk * 8192 + h * 2048>(sB + buf * kOpStageBytes + bt_rd[blk]);
+    }
+  };
+  auto tie_frags = [&](Frags<MODE>& f) {
+    if constexpr (MODE == kNT) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i) tie(f.a[i]);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) tie(f.b[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        tie(f.a[i][0]);
+        tie(f.a[i][1]);
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        tie(f.b[i][0]);
+        tie(f.b[i][1]);
+      }
+    }
+  };
+
+  f32x16_t acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+
+  auto mfma_one = [&](const Frags<MODE>& f, auto q_c) {
+    constexpr int q = decltype(q_c)::value, mi = q / NI, ni = q % NI;
+    if constexpr (MODE == kNT)
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
+    else
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join(f.a[mi][0], f.a[mi][1]), join(f.b[ni][0], f.b[ni][1]),
+                                                            acc[mi][ni], 0, 0, 0);
+  };
+
+  // DMA of one stage: loads 0..3 the A operand, 4..7 the B operand (this wave's
+  // four 1 KB pieces of each)
+  struct StageLoads {
+    __amdgpu_buffer_rsrc_t ra, rb;
+    uint32_t la, lb;
+  };
+  auto stage_loads = [&](int s) {
+    const int buf = s % kStages;
+    return StageLoads{stage_rsrc(opa, s), stage_rsrc(opb, s), sA + buf * kOpStageBytes,
+                      sB + buf * kOpStageBytes};
+  };
+  auto dma_one = [&](const StageLoads& st, auto j_c) {
+    constexpr int j = decltype(j_c)::value;
+    if constexpr (j < 4) dma16(st.ra, opa.voff[j], st.la + (wave * 4 + j) * 1024);
+    else dma16(st.rb, opb.voff[j - 4], st.lb + (wave * 4 + (j - 4)) * 1024);
+  };
+  auto wait_stage = [&](int s) {
+    const int after = min(kStages - 2, ksteps - 1 - s);
+    if (after >= 2) wait_vmcnt<2 * PER>();
+    else if (after == 1) wait_vmcnt<PER>();
+    else wait_vmcnt<0>();
+  };
+  using K0 = std::integral_constant<int, 0>;
+  using K1 = std::integral_constant<int, 1>;
+  constexpr int NM = MI * NI;
+  // reads per MFMA: all of a slice's reads go out in the first three quarters of
+  // the slice, so the last has a quarter slice of MFMAs to land
+  constexpr int RPM = (R + (NM * 3 / 4) - 1) / (NM * 3 / 4);
+
+  // One stage, as in the forward kernel: slice 0 carries slice 1's reads, one per
+  // MFMA; the stage barrier; slice 1 carries the next stage's slice-0 reads, one
+  // per MFMA, and the DMA of stage ks + kStages, one per two MFMAs.
+  Frags<MODE> f0, f1;
+  auto stage = [&](int ks, auto dma_c, auto more_c) {
+    constexpr bool DMA = decltype(dma_c)::value, MORE = decltype(more_c)::value;
+    const int buf = ks % kStages;
+    wait_lgkmcnt<0>();
+    tie_frags(f0);
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, NM>([&](auto q_c) {
+      constexpr int q = decltype(q_c)::value;
+      mfma_one(f0, q_c);
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<(q * RPM < R ? q * RPM : R), ((q + 1) * RPM < R ? (q + 1) * RPM : R)>(
+          [&](auto r) { read_one(f1, buf, K1{}, r); });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    wait_lgkmcnt<0>();
+    tie_frags(f1);
+    if constexpr (MORE) {
+      wait_stage(ks + 1);
+      __builtin_amdgcn_s_barrier();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    StageLoads st;
+    if constexpr (DMA) st = stage_loads(ks + kStages);
+    const int nbuf = (ks + 1) % kStages;
+    static_for<0, NM>([&](auto q_c) {
+      constexpr int q = decltype(q_c)::value;
+      mfma_one(f1, q_c);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (MORE)
+        static_for<(q * RPM < R ? q * RPM : R), ((q + 1) * RPM < R ? (q + 1) * RPM : R)>(
+            [&](auto r) { read_one(f0, nbuf, K0{}, r); });
+      if constexpr (DMA && q % 2 == 0 && q / 2 < PER) dma_one(st, std::integral_constant<int, q / 2>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  if (ksteps > 0) {
+    for (int s = 0; s < kStages - 1 && s < ksteps; ++s) {
+      const StageLoads st = stage_loads(s);
+      static_for<0, PER>([&](auto j) { dma_one(st, j); });
+    }
+    wait_stage(0);
+    __builtin_amdgcn_s_barrier();
+    if (kStages - 1 < ksteps) {
+      const StageLoads st = stage_loads(kStages - 1);
+      static_for<0, PER>([&](auto j) { dma_one(st, j); });
+    }
+    static_for<0, R>([&](auto r) { read_one(f0, 0, K0{}, r); });
+    int ks = 0;
+    for (; ks + kStages < ksteps; ++ks) stage(ks, std::true_type{}, std::true_type{});
+    for (; ks + 1 < ksteps; ++ks) stage(ks, std::false_type{}, std::true_type{});
+    stage(ks, std::false_type{}, std::false_type{});
+  }
+
+  // ---- epilogue: C is c_rows x c_cols (row stride ldc) at the tile origin --------
+  const __amdgpu_buffer_rsrc_t rc =
+      make_rsrc(C, static_cast<uint32_t>(c_rows) * static_cast<uint32_t>(ldc) * 2u);
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) {
+    const int col = wn * 128 + ni * 32 + l31;
+    const uint32_t coff = col < c_cols ? static_cast<uint32_t>(col) * 2u : 0x80000000u;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      if constexpr (EPI == kSwigluBwd) {
+        // acc = dH at (row, f = col); G and U of the same element from gu [rows][2 N]
+        // (ldc = 2 N); dG goes to column f and dU to column N + f of C
+        const __amdgpu_buffer_rsrc_t rg = make_rsrc(gu, static_cast<uint32_t>(c_rows) * static_cast<uint32_t>(ldc) * 2u);
+        const uint32_t uoff = col < c_cols ? static_cast<uint32_t>(up_off + col) * 2u : 0x80000000u;
+        float g[16], u[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * 128 + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const uint32_t ro = static_cast<uint32_t>(row) * static_cast<uint32_t>(ldc) * 2u;
+          g[r] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rg, static_cast<int>(ro + coff), 0, 0));
+          u[r] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rg, static_cast<int>(ro + uoff), 0, 0));
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * 128 + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const uint32_t ro = static_cast<uint32_t>(row) * static_cast<uint32_t>(ldc) * 2u;
+          const float dh = acc[mi][ni][r];
+          const float s = sigmoid_fast(g[r]);
+          const float dg = dh * u[r] * (s * (1.0f + g[r] * (1.0f - s)));
+          const float du = dh * g[r] * s;
+          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(dg), rc, static_cast<int>(ro + coff), 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(du), rc, static_cast<int>(ro + uoff), 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * 128 + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const uint32_t ro = static_cast<uint32_t>(row) * static_cast<uint32_t>(ldc) * 2u;
+          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(acc[mi][ni][r]), rc, static_cast<int>(ro + coff), 0,
+                                                0);
+        }
+      }
+    }
+  }
+}
+
+// NT: C[rows, N] = A[rows, K] @ B_e[N, K]^T over row tiles of each local expert.
+// EPI = kSwigluBwd: A = dY, B = W_dn (N = d_ff, K = d), C = [dG | dU] with row
+// stride 2 N, gu = [G | U] of the same rows.
+template <int EPI>
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_nt_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
+    const uint16_t* __restrict__ gu, const int32_t* __restrict__ offsets, int e_begin, int e_loc, int K, int N,
+    int ldc, int n_max) {
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[kStages * 2 * 256 * kBK];
+  __shared__ TileMap tm;
+  build_tile_map<256>(tm, offsets, e_begin, e_loc, n_max);
+  const int n_tiles = (N + 255) / 256;
+  const int total = uniform(tm.mstart[e_loc]) * n_tiles;
+  const int lane = lane_id();
+  const int wave = uniform(static_cast<int>(threadIdx.x) / kWave);
+  for (int tile = xcd_remap(blockIdx.x, gridDim.x); tile < total; tile += gridDim.x) {
+    const TileCoord tc = find_tile(tm, tile, n_tiles, e_loc);
+    const int row0 = uniform(tm.rstart[tc.e]) + tc.mt * 256;
+    const int rows = min(256, uniform(tm.rstart[tc.e + 1]) - row0);
+    const int n0 = tc.nt * 256;
+    const uint16_t* Bexp = B + static_cast<int64_t>(tc.e) * N * K;
+    const Operand opa = krows_operand(A + static_cast<int64_t>(row0) * K, rows, K, wave, lane);
+    const Operand opb = krows_operand(Bexp + static_cast<int64_t>(n0) * K, N - n0, K, wave, lane);
+    bwd_tile<kNT, EPI>(smem, opa, opb, K / kBK, C + static_cast<int64_t>(row0) * ldc + n0, rows, N - n0, ldc,
+                       EPI == kSwigluBwd ? gu + static_cast<int64_t>(row0) * ldc + n0 : nullptr, N);
+    __builtin_amdgcn_s_barrier();
+  }
+}
+
+// TN: dW_e[M, N] = A_e^T @ B_e with A = src_a [rows][M], B = src_b [rows][N]
+// over each local expert's rows (K = its row count; none gives zeros).
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_tn_kernel(
+    const uint16_t* __restrict__ src_a, const uint16_t* __restrict__ src_b, uint16_t* __restrict__ dW,
+    const int32_t* __restrict__ offsets, int e_begin, int e_loc, int M, int N, int n_max) {
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[kStages * 2 * 256 * kBK];
+  const int m_tiles = (M + 255) / 256, n_tiles = (N + 255) / 256;
+  const int per_e = m_tiles * n_tiles;
+  const int total = e_loc * per_e;
+  const int lane = lane_id();
+  const int wave = uniform(static_cast<int>(threadIdx.x) / kWave);
+  const int base = offsets[e_begin];
+  for (int tile = xcd_remap(blockIdx.x, gridDim.x); tile < total; tile += gridDim.x) {
+    const int e = tile / per_e;
+    const int rem = tile - e * per_e;
+    const int mt = rem / n_tiles, nt = rem - mt * n_tiles;
+    const int r0 = uniform(min(offsets[e_begin + e] - base, n_max));
+    const int rows = uniform(min(offsets[e_begin + e + 1] - base, n_max)) - r0;
+    const int m0 = mt * 256, n0 = nt * 256;
+    const Operand opa = kmajor_operand(src_a + static_cast<int64_t>(r0) * M, rows, M, m0, wave, lane);
+    const Operand opb = kmajor_operand(src_b + static_cast<int64_t>(r0) * N, rows, N, n0, wave, lane);
+    bwd_tile<kTN, kPlain>(smem, opa, opb, (rows + kBK - 1) / kBK,
+                          dW + static_cast<int64_t>(e) * M * N + static_cast<int64_t>(m0) * N + n0, M - m0, N - n0, N,
+                          nullptr, 0);
+    __builtin_amdgcn_s_barrier();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_grouped_gemm_nt(const void* a, const void* b, void* c, const void* gu, const int32_t* offsets,
+                                  int e_begin, int e_loc, int K, int N, int ldc, int64_t n_max, bool swiglu_bwd,
+                                  int grid, hipStream_t stream) {
+  if (swiglu_bwd) {
+    hipLaunchKernelGGL(grouped_gemm_nt_kernel<kSwigluBwd>, dim3(grid), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), static_cast<uint16_t*>(c),
+                       static_cast<const uint16_t*>(gu), offsets, e_begin, e_loc, K, N, ldc, static_cast<int>(n_max));
+  } else {
+    hipLaunchKernelGGL(grouped_gemm_nt_kernel<kPlain>, dim3(grid), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), static_cast<uint16_t*>(c),
+                       nullptr, offsets, e_begin, e_loc, K, N, ldc, static_cast<int>(n_max));
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm_tn(const void* src_a, const void* src_b, void* dw, const int32_t* offsets,
+                                  int e_begin, int e_loc, int M, int N, int64_t n_max, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(grouped_gemm_tn_kernel, dim3(grid), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(src_a), static_cast<const uint16_t*>(src_b),
+                     static_cast<uint16_t*>(dw), offsets, e_begin, e_loc, M, N, static_cast<int>(n_max));
+  return hipGetLastError();
+}
+
+}  // namespace moe

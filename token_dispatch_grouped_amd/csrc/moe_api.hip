@@ -34,6 +34,18 @@ int64_t n_max_of(const moe_shape* s) {
   return s->T * (s->k < e_loc ? s->k : e_loc);
 }
 
+constexpr size_t kWsAlign = 256;
+size_t align_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
+// workspace of moe_grouped_gemm_backward: x_perm [N_max, d], gu and d_gu [N_max, 2 d_ff]
+size_t backward_ws(const moe_shape* s, size_t* off_gu, size_t* off_dgu) {
+  const size_t n = static_cast<size_t>(n_max_of(s));
+  const size_t xp = align_up(n * static_cast<size_t>(s->d) * 2);
+  const size_t g = align_up(n * static_cast<size_t>(s->d_ff) * 2 * 2);
+  if (off_gu) *off_gu = xp;
+  if (off_dgu) *off_dgu = xp + g;
+  return xp + 2 * g;
+}
+
 }  // namespace
 
 extern "C" {
@@ -171,6 +183,113 @@ moe_status moe_combine(const moe_shape* s, moe_dtype dt, const void* y, const in
   if (y == nullptr || pair_pos == nullptr || topk_w == nullptr || out == nullptr) return MOE_EINVAL;
   return from_hip(moe::launch_combine(y, pair_pos, topk_w, out, s->T, s->k, s->d, n_max_of(s),
                                       dt == MOE_BF16, stream));
+}
+
+// ------------------------------------------------------------------ backward
+
+moe_status moe_combine_backward(const moe_shape* s, moe_dtype dt, const void* d_out, const void* y,
+                                const int32_t* pair_pos, const float* topk_w, void* d_y, float* d_topk_w,
+                                hipStream_t stream) {
+  const moe_status st = check_shape(s, true);
+  if (st != MOE_OK) return st;
+  if (!valid_dtype(dt)) return MOE_EINVAL;
+  if (s->T == 0) return MOE_OK;
+  if (d_out == nullptr || y == nullptr || pair_pos == nullptr || topk_w == nullptr || d_y == nullptr ||
+      d_topk_w == nullptr)
+    return MOE_EINVAL;
+  return from_hip(moe::launch_combine_backward(d_out, y, pair_pos, topk_w, d_y, d_topk_w, s->T, s->k, s->d,
+                                               n_max_of(s), dt == MOE_BF16, stream));
+}
+
+size_t moe_grouped_gemm_backward_workspace_bytes(const moe_shape* s, moe_dtype dt) {
+  if (check_shape(s, true) != MOE_OK || dt != MOE_BF16) return 0;
+  return backward_ws(s, nullptr, nullptr);
+}
+
+moe_status moe_grouped_gemm_backward(const moe_shape* s, moe_dtype dt, const void* x, const int32_t* perm,
+                                     const int32_t* offsets, const void* w_gate_up, const void* w_down,
+                                     const void* h, const void* d_y, void* d_x_perm, void* d_w_gate_up,
+                                     void* d_w_down, void* workspace, hipStream_t stream) {
+  const moe_status st = check_shape(s, true);
+  if (st != MOE_OK) return st;
+  if (!valid_dtype(dt)) return MOE_EINVAL;
+  if (offsets == nullptr || w_gate_up == nullptr || w_down == nullptr || d_w_gate_up == nullptr ||
+      d_w_down == nullptr)
+    return MOE_EINVAL;
+  // with no tokens only the (zero) weight gradients are written
+  if (s->T > 0 && (x == nullptr || perm == nullptr || h == nullptr || d_y == nullptr || d_x_perm == nullptr ||
+                   workspace == nullptr))
+    return MOE_EINVAL;
+  // the pipelined bf16 kernels only: K in whole 32-wide stages
+  if (dt != MOE_BF16 || s->d % 32 != 0 || s->d_ff % 32 != 0) return MOE_EUNSUPPORTED;
+  const int64_t n_max = n_max_of(s);
+  // 32-bit buffer offsets: the widest activation block of an expert, x, and a weight matrix
+  const int64_t widest = s->d > 2 * static_cast<int64_t>(s->d_ff) ? s->d : 2 * static_cast<int64_t>(s->d_ff);
+  if (n_max * 2 * widest + 64 > INT32_MAX || s->T * static_cast<int64_t>(s->d) * 2 + 64 > INT32_MAX ||
+      (static_cast<int64_t>(s->d) + 64) * 2 * s->d_ff * 2 > INT32_MAX ||
+      (static_cast<int64_t>(s->d_ff) + 64) * s->d * 2 > INT32_MAX)
+    return MOE_EUNSUPPORTED;
+  const int e_loc = s->e_end - s->e_begin;
+  const int d = s->d, d_ff = s->d_ff;
+  size_t off_gu = 0, off_dgu = 0;
+  backward_ws(s, &off_gu, &off_dgu);
+  char* ws = static_cast<char*>(workspace);
+  void* x_perm = ws;
+  void* gu = ws + off_gu;
+  void* d_gu = ws + off_dgu;
+  hipError_t e = hipSuccess;
+  if (n_max > 0) {
+    // the rows of the local pairs, then their gate/up pre-activations (recomputed, not stored by the forward)
+    e = moe::launch_gather_rows(x, static_cast<size_t>(d) * 2, perm, offsets, x_perm, s->k, s->e_begin, s->e_end,
+                                n_max, stream);
+    if (e == hipSuccess)
+      e = moe::launch_grouped_gemm_plain(x_perm, w_gate_up, gu, offsets, s->e_begin, e_loc, d, 2 * d_ff, 2 * d_ff,
+                                         n_max, moe::grouped_gemm_grid(n_max, e_loc, (2 * d_ff + 255) / 256), stream);
+    // [dG | dU] from dH = dY @ W_dn^T and [G | U]
+    if (e == hipSuccess)
+      e = moe::launch_grouped_gemm_nt(d_y, w_down, d_gu, gu, offsets, s->e_begin, e_loc, d, d_ff, 2 * d_ff, n_max,
+                                      true, moe::grouped_gemm_grid(n_max, e_loc, (d_ff + 255) / 256), stream);
+    // dX_perm = [dG | dU] @ W_gu^T
+    if (e == hipSuccess)
+      e = moe::launch_grouped_gemm_nt(d_gu, w_gate_up, d_x_perm, nullptr, offsets, s->e_begin, e_loc, 2 * d_ff, d,
+                                      d, n_max, false, moe::grouped_gemm_grid(n_max, e_loc, (d + 255) / 256), stream);
+  }
+  // weight gradients over each expert's rows (an expert without rows gets zeros)
+  const int cus = moe::device_cu_count();
+  auto tn_grid = [&](int M, int N) {
+    const int64_t tiles = static_cast<int64_t>(e_loc) * ((M + 255) / 256) * ((N + 255) / 256);
+    int64_t g = tiles < cus ? tiles : cus;
+    if (g > 8) g &= ~int64_t{7};
+    return static_cast<int>(g < 1 ? 1 : g);
+  };
+  if (e == hipSuccess)
+    e = moe::launch_grouped_gemm_tn(h, d_y, d_w_down, offsets, s->e_begin, e_loc, d_ff, d, n_max, tn_grid(d_ff, d),
+                                    stream);
+  if (e == hipSuccess)
+    e = moe::launch_grouped_gemm_tn(x_perm, d_gu, d_w_gate_up, offsets, s->e_begin, e_loc, d, 2 * d_ff, n_max,
+                                    tn_grid(d, 2 * d_ff), stream);
+  return from_hip(e);
+}
+
+moe_status moe_dispatch_backward(const moe_shape* s, moe_dtype dt, const void* d_x_perm, const int32_t* pair_pos,
+                                 void* d_x, hipStream_t stream) {
+  const moe_status st = check_shape(s, true);
+  if (st != MOE_OK) return st;
+  if (!valid_dtype(dt)) return MOE_EINVAL;
+  if (s->T == 0) return MOE_OK;
+  if (d_x_perm == nullptr || pair_pos == nullptr || d_x == nullptr) return MOE_EINVAL;
+  return from_hip(moe::launch_combine(d_x_perm, pair_pos, nullptr, d_x, s->T, s->k, s->d, n_max_of(s),
+                                     dt == MOE_BF16, stream));
+}
+
+moe_status moe_route_topk_backward(const moe_shape* s, const int32_t* topk_idx, const float* topk_w,
+                                   const float* d_topk_w, float* d_logits, hipStream_t stream) {
+  const moe_status st = check_shape(s, false);
+  if (st != MOE_OK) return st;
+  if (s->T == 0) return MOE_OK;
+  if (topk_idx == nullptr || topk_w == nullptr || d_topk_w == nullptr || d_logits == nullptr) return MOE_EINVAL;
+  if (s->T * static_cast<int64_t>(s->E) > (int64_t{1} << 40)) return MOE_EUNSUPPORTED;
+  return from_hip(moe::launch_route_topk_backward(topk_idx, topk_w, d_topk_w, d_logits, s->T, s->E, s->k, stream));
 }
 
 }  // extern "C"

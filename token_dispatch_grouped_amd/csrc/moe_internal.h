@@ -78,7 +78,33 @@ hipError_t launch_grouped_gemm_f32(const float* x_perm, const int32_t* offsets, 
                                    const float* w_dn, float* h, float* y, int d, int d_ff,
                                    int e_begin, int e_loc, int64_t n_max, hipStream_t stream);
 
+// w == nullptr: unit weights (the gradient of the row gather)
 hipError_t launch_combine(const void* y, const int32_t* pair_pos, const float* w, void* out,
                           int64_t T, int k, int d, int64_t n_max, bool bf16, hipStream_t stream);
+
+// x_perm rows [0, N_loc) = x[perm[offsets[e_begin] + r] / k]
+hipError_t launch_gather_rows(const void* x, size_t row_bytes, const int32_t* perm, const int32_t* offsets,
+                              void* x_perm, int k, int e_begin, int e_end, int64_t n_max, hipStream_t stream);
+
+// C[rows, N] = A[rows, K] @ B_e[K, N] (N-contiguous weights, row stride ldb) per local expert
+hipError_t launch_grouped_gemm_plain(const void* a, const void* b, void* c, const int32_t* offsets, int e_begin,
+                                     int e_loc, int K, int N, int ldb, int64_t n_max, int grid, hipStream_t stream);
+// C[rows, N] = A[rows, K] @ B_e[N, K]^T (K-contiguous weights); with swiglu_bwd, A = dY, B = W_dn and C receives
+// [dG | dU] (row stride ldc = 2 N) from the [G | U] rows in gu
+hipError_t launch_grouped_gemm_nt(const void* a, const void* b, void* c, const void* gu, const int32_t* offsets,
+                                  int e_begin, int e_loc, int K, int N, int ldc, int64_t n_max, bool swiglu_bwd,
+                                  int grid, hipStream_t stream);
+// dW_e[M, N] = A_e^T @ B_e over each local expert's rows (A [rows][M], B [rows][N])
+hipError_t launch_grouped_gemm_tn(const void* src_a, const void* src_b, void* dw, const int32_t* offsets,
+                                  int e_begin, int e_loc, int M, int N, int64_t n_max, int grid, hipStream_t stream);
+// persistent-grid size for a row-tiled grouped GEMM with n_tiles column tiles
+int grouped_gemm_grid(int64_t n_max, int e_loc, int n_tiles);
+int device_cu_count();
+
+hipError_t launch_combine_backward(const void* d_out, const void* y, const int32_t* pair_pos, const float* w,
+                                   void* d_y, float* d_w, int64_t T, int k, int d, int64_t n_max, bool bf16,
+                                   hipStream_t stream);
+hipError_t launch_route_topk_backward(const int32_t* idx, const float* w, const float* d_w, float* d_logits,
+                                      int64_t T, int E, int k, hipStream_t stream);
 
 }  // namespace moe
