@@ -136,6 +136,9 @@ def main() -> int:
     ap.add_argument("--path", choices=["fused", "staged"], default="fused",
                     help="fused: dispatch indices only, the gate/up GEMM gathers rows from x; "
                          "staged: dispatch gathers rows into x_perm first")
+    ap.add_argument("--train", action="store_true",
+                    help="a step is the forward and then the backward of the layer (seeded d_out); the "
+                         "roofline object then covers moe_grouped_gemm_backward")
     ap.add_argument("--graph", action="store_true",
                     help="record one step in a HIP graph and time graph replays (the GEMM roofline "
                          "then comes from an eager pass after the timed replays)")
@@ -204,15 +207,54 @@ def main() -> int:
             moe.grouped_gemm(disp.x_perm, disp.offsets, dgu, ddn, w.T, w.k, w.E, w.e_begin, w.e_end,
                              h=h, y=y, stream=cur())
 
+    train = args.train
+    if train:
+        if w.dtype != "bf16" or not fused:
+            print("--train runs the fused bf16 path", file=sys.stderr)
+            return 2
+        rng = np.random.default_rng(w.seed + 500)
+        d_out = to_dev(mi.f32_to_bf16_bits(rng.standard_normal((w.T, w.d)).astype(np.float32)), "bf16")
+        d_y = torch.empty((w.n_max, w.d), dtype=dx.dtype, device=dev)
+        d_w = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
+        d_xp = torch.empty((w.n_max, w.d), dtype=dx.dtype, device=dev)
+        d_wgu, d_wdn = torch.empty_like(dgu), torch.empty_like(ddn)
+        d_x = torch.empty((w.T, w.d), dtype=dx.dtype, device=dev)
+        d_logits = torch.empty((w.T, w.E), dtype=torch.float32, device=dev)
+        ws_bytes = moe.grouped_gemm_backward_workspace_bytes(w.T, w.d, w.d_ff, w.E, w.k, w.e_begin, w.e_end)
+        bws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def bwd_gemm():
+        moe.grouped_gemm_backward(dx, disp.perm, disp.offsets, dgu, ddn, h, d_y, w.k, w.E, w.e_begin, w.e_end,
+                                  d_x_perm=d_xp, d_w_gate_up=d_wgu, d_w_down=d_wdn, workspace=bws, stream=cur())
+
+    # the calls of one step, in order: (name, call)
+    calls = [
+        ("route_topk", lambda: moe.route_topk(dl, w.k, idx, wts, stream=cur())),
+        ("dispatch", lambda: moe.dispatch(dx, idx, w.E, w.e_begin, w.e_end, out=disp, stream=cur(),
+                                          gather=not fused)),
+        ("grouped_gemm", gemm),
+        ("combine", lambda: moe.combine(y, disp.pair_pos, wts, w.T, w.k, w.E, w.e_begin, w.e_end, out=out,
+                                        stream=cur())),
+    ]
+    if train:
+        calls += [
+            ("combine_backward", lambda: moe.combine_backward(d_out, y, disp.pair_pos, wts, w.T, w.k, w.E, w.e_begin,
+                                                              w.e_end, d_y=d_y, d_topk_w=d_w, stream=cur())),
+            ("grouped_gemm_backward", bwd_gemm),
+            ("dispatch_backward", lambda: moe.dispatch_backward(d_xp, disp.pair_pos, w.T, w.k, w.E, w.e_begin,
+                                                                w.e_end, d_x=d_x, stream=cur())),
+            ("route_topk_backward", lambda: moe.route_topk_backward(idx, wts, d_w, w.E, d_logits=d_logits,
+                                                                    stream=cur())),
+        ]
+    timed = "grouped_gemm_backward" if train else "grouped_gemm"  # the roofline's kernel
+
     def step(i=None):
-        moe.route_topk(dl, w.k, idx, wts, stream=cur())
-        moe.dispatch(dx, idx, w.E, w.e_begin, w.e_end, out=disp, stream=cur(), gather=not fused)
-        if i is not None:
-            ev[i][0].record(cur())
-        gemm()
-        if i is not None:
-            ev[i][1].record(cur())
-        moe.combine(y, disp.pair_pos, wts, w.T, w.k, w.E, w.e_begin, w.e_end, out=out, stream=cur())
+        for name, call in calls:
+            if i is not None and name == timed:
+                ev[i][0].record(cur())
+            call()
+            if i is not None and name == timed:
+                ev[i][1].record(cur())
 
     for _ in range(args.warmup):
         step()
@@ -252,11 +294,19 @@ def main() -> int:
         torch.cuda.synchronize()
     gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
-    flops = 6.0 * n_loc * w.d * w.d_ff  # gate/up (4 N d d_ff) + down (2 N d d_ff)
+    # forward: gate/up (4 N d d_ff) + down (2 N d d_ff); backward: recomputed gate/up (4), dH (2),
+    # dX (4), dW_dn (2), dW_gu (4)
+    flops = (16.0 if train else 6.0) * n_loc * w.d * w.d_ff
     b = 2 if w.dtype == "bf16" else 4
-    # weights of every active local expert once, one activation row per local pair and H read
-    # once, H and Y written once
-    gemm_bytes = 3.0 * active * w.d * w.d_ff * b + 2.0 * n_loc * (w.d + w.d_ff) * b
+    # forward: weights of every active local expert once, one activation row per local pair and
+    # H read once, H and Y written once. backward: W_gu read twice and W_dn once, both weight
+    # gradients written once (8 d d_ff per active expert); per local row, the d-wide blocks
+    # moved 7 times (x, x_perm, dY twice, dX) and the d_ff-wide ones 11 times (gate/up written
+    # and read, their gradient written and read twice, H read)
+    if train:
+        gemm_bytes = 8.0 * active * w.d * w.d_ff * b + n_loc * (7.0 * w.d + 11.0 * w.d_ff) * b
+    else:
+        gemm_bytes = 3.0 * active * w.d * w.d_ff * b + 2.0 * n_loc * (w.d + w.d_ff) * b
     peak_flops = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
     t_gemm = gemm_ms * 1e-3
     # the bound is whichever of MFMA time and HBM time is longer at peak
@@ -266,14 +316,16 @@ def main() -> int:
         bound = "mfma" if w.dtype == "bf16" else "alu"
         achieved, peak, unit = flops / t_gemm / 1e12, peak_flops, "TFLOP/s"
     roofline = {
-        "kernel": ("moe_grouped_gemm_gather" if fused else "moe_grouped_gemm")
-                  + " (gate/up+SwiGLU launch, then down launch)",
+        "kernel": ("moe_grouped_gemm_backward (row gather, gate/up recompute, dH+SwiGLU backward, dX, "
+                   "dW_down, dW_gate_up launches)" if train else
+                   ("moe_grouped_gemm_gather" if fused else "moe_grouped_gemm")
+                   + " (gate/up+SwiGLU launch, then down launch)"),
         "bound": bound,
         "achieved": round(achieved, 2),
         "peak": peak,
         "unit": unit,
         "frac": round(achieved / peak, 4),
-        "traffic": stored_traffic(w.name),
+        "traffic": None if train else stored_traffic(w.name),
         "flops_per_launch": flops,
         "algorithmic_bytes_per_launch": gemm_bytes,
         "avg_ms": round(gemm_ms, 4),
@@ -294,28 +346,23 @@ def main() -> int:
         "config": {"workload": w.name, "T": w.T, "d": w.d, "d_ff": w.d_ff, "E": w.E, "k": w.k,
                    "local_experts": [w.e_begin, w.e_end], "N_loc": n_loc, "active_local_experts": active,
                    "parallelism": "one rank's share on 1 GPU", "path": args.path,
-                   "launch": "hip graph" if args.graph else "eager"},
+                   "launch": "hip graph" if args.graph else "eager",
+                   "step": "forward + backward" if args.train else "forward"},
         "local_pairs_per_s": round(n_loc / (ms_step * 1e-3), 1),
         "roofline": roofline,
         "cpu_baseline": None,
     }
-    # per entry point, in a separate untimed pass: events between the four calls
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # per entry point, in a separate untimed pass: events between the calls
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
     for i in range(args.steps):
         e = evs[i]
         e[0].record(cur())
-        moe.route_topk(dl, w.k, idx, wts, stream=cur())
-        e[1].record(cur())
-        moe.dispatch(dx, idx, w.E, w.e_begin, w.e_end, out=disp, stream=cur(), gather=not fused)
-        e[2].record(cur())
-        gemm()
-        e[3].record(cur())
-        moe.combine(y, disp.pair_pos, wts, w.T, w.k, w.E, w.e_begin, w.e_end, out=out, stream=cur())
-        e[4].record(cur())
+        for j, (_, call) in enumerate(calls):
+            call()
+            e[j + 1].record(cur())
     torch.cuda.synchronize()
-    parts = ["route_topk", "dispatch", "grouped_gemm", "combine"]
-    result["entry_point_ms"] = {p: round(float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])), 4)
-                                for j, p in enumerate(parts)}
+    result["entry_point_ms"] = {name: round(float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])), 4)
+                                for j, (name, _) in enumerate(calls)}
     if args.clock_seconds > 0:
         result["sclk_mhz"] = sample_sclk(step, args.clock_seconds, torch)
     del dgu, ddn

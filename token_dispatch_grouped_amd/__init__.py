@@ -325,8 +325,13 @@ def combine_backward(d_out, y, pair_pos, topk_w, T: int, k: int, E: int, e_begin
     return d_y, d_topk_w
 
 
+def grouped_gemm_backward_workspace_bytes(T: int, d: int, d_ff: int, E: int, k: int, e_begin: int, e_end: int) -> int:
+    s = shape(T, d, d_ff, E, k, e_begin, e_end)
+    return int(_load().moe_grouped_gemm_backward_workspace_bytes(ctypes.byref(s), MOE_BF16))
+
+
 def grouped_gemm_backward(x, perm, offsets, w_gate_up, w_down, h, d_y, k: int, E: int, e_begin: int, e_end: int,
-                          d_x_perm=None, d_w_gate_up=None, d_w_down=None, stream=None):
+                          d_x_perm=None, d_w_gate_up=None, d_w_down=None, workspace=None, stream=None):
     """(d_x_perm, d_w_gate_up, d_w_down): the gradient of the grouped expert FFN."""
     torch = _torch()
     _dev(x, perm, offsets, w_gate_up, w_down, h, d_y)
@@ -340,8 +345,10 @@ def grouped_gemm_backward(x, perm, offsets, w_gate_up, w_down, h, d_y, k: int, E
         d_w_gate_up = torch.empty_like(w_gate_up)
     if d_w_down is None:
         d_w_down = torch.empty_like(w_down)
-    ws_bytes = _load().moe_grouped_gemm_backward_workspace_bytes(ctypes.byref(s), dt)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device) if ws_bytes else None
+    ws = workspace
+    if ws is None:
+        ws_bytes = _load().moe_grouped_gemm_backward_workspace_bytes(ctypes.byref(s), dt)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device) if ws_bytes else None
     _check(_load().moe_grouped_gemm_backward(ctypes.byref(s), dt, _ptr(x), _ptr(perm), _ptr(offsets),
                                              _ptr(w_gate_up), _ptr(w_down), _ptr(h), _ptr(d_y), _ptr(d_x_perm),
                                              _ptr(d_w_gate_up), _ptr(d_w_down), _ptr(ws), _stream(stream)),
