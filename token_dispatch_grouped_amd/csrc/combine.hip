@@ -19,7 +19,10 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kChunks = 4;  // 16-byte chunks per lane per pass
+#ifndef MOE_COMBINE_CHUNKS
+#define MOE_COMBINE_CHUNKS 8
+#endif
+constexpr int kChunks = MOE_COMBINE_CHUNKS;  // 16-byte chunks per lane per pass
 
 template <bool BF16>
 struct Vec;
