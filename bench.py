@@ -31,7 +31,7 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0
 # Sources that decide the grouped GEMM's machine code; a stored traffic figure is
 # reported only while they are unchanged since its counters were taken.
-GEMM_SOURCES = ["gemm_common.h", "moe_internal.h", "grouped_gemm.hip", "grouped_gemm_lds.hip"]
+GEMM_SOURCES = ["gemm_common.h", "lds_pipe.h", "moe_internal.h", "grouped_gemm.hip", "grouped_gemm_lds.hip"]
 
 
 def host_cores() -> int:
