@@ -310,3 +310,27 @@ def test_fused_gemm_rejects_unsupported_shapes():
     with pytest.raises(moe.MoeError) as e:
         moe.layer(x, logits, wgu, wdn, w.k, w.e_begin, w.e_end, fused=True)
     assert e.value.status == moe.MOE_EUNSUPPORTED
+
+
+# ----------------------------------------------------------------------------- decode-shaped, skewed
+
+DECODE_SHAPED = [
+    # few rows per local expert on average, but skewed routing puts hundreds of rows
+    # on a few experts (several row tiles each, next to many one-row experts)
+    mi.Workload("decode_uneven", 200, 256, 192, 64, 8, 0, 64, "bf16", 28, 2.0),
+    mi.Workload("decode_uneven_share", 300, 320, 160, 128, 4, 32, 96, "bf16", 29, 2.0),
+]
+
+
+@pytest.mark.parametrize("w", DECODE_SHAPED, ids=[w.name for w in DECODE_SHAPED])
+def test_decode_shaped_skewed_layer_matches_oracle(w):
+    res, ref = _layer_case(w)
+    counts = np.diff(ref["offsets"])[w.e_begin:w.e_end]
+    assert counts.max() > 64
+    logits = mi.router_logits(w)
+    x = mi.hidden_states(w)
+    wgu, wdn = mi.expert_weights(w)
+    fused = moe.layer(g.to_dev(x, w.dtype), g.to_dev(logits, "f32"), g.to_dev(wgu, w.dtype),
+                      g.to_dev(wdn, w.dtype), w.k, w.e_begin, w.e_end, fused=True)
+    torch.cuda.synchronize()
+    assert torch.equal(fused["out"], res["out"])
