@@ -31,8 +31,9 @@ using namespace gemm;
 
 constexpr int kBK = 32;
 constexpr int kStages = 4;
-constexpr int kOpStageBytes = 256 * kBK * 2;  // 16 KB per operand per stage
-constexpr int MI = 4, NI = 4, PER = 8;        // blocks per wave; DMA loads per wave per stage
+constexpr int kOpStageBytes = 256 * kBK * 2;  // 16 KB: a 256-row (or 256-column) operand stage
+constexpr int kNTAStageBytes = 288 * kBK * 2; // 18 KB: NT activation stage, room for a 288-row tile
+constexpr int MI = 4, NI = 4;                 // 32 x 32 blocks per wave
 
 enum Mode { kNT = 0, kTN = 1 };
 enum Epi { kPlain = 0, kSwigluBwd = 1 };
@@ -41,7 +42,7 @@ template <int MODE>
 struct Frags;
 template <>
 struct Frags<kNT> {
-  bf16x8_t a[MI], b[NI];
+  bf16x8_t a[MI + 1], b[NI];  // a[MI]: the shared extra row block of a 288-row tile
 };
 template <>
 struct Frags<kTN> {
@@ -53,19 +54,25 @@ struct Operand {
   const uint16_t* base;  // first element of the tile's rows (KROWS) or k-rows (KMAJOR) at stage 0
   uint32_t bytes;        // bytes from base that are valid (past them: zeros)
   uint32_t stage_step;   // bytes base advances per stage
-  uint32_t voff[4];      // per-lane byte offsets of this wave's 4 loads
+  uint32_t voff[5];      // per-lane byte offsets of this wave's loads (4, or 5 for 288 rows)
+  int slot[5];           // 1 KB LDS slot of each load inside the stage
 };
 
-// KROWS operand ([row][K], K contiguous): load j of a stage covers rows
-// 16j..16j+15, lane L row 16j + L/4, 16-byte chunk (L & 3) ^ ((row >> 2) & 3).
+// KROWS operand ([row][K], K contiguous) of ROWS rows (256 or 288): load j of a
+// stage covers rows 16j..16j+15, lane L row 16j + L/4, 16-byte chunk
+// (L & 3) ^ ((row >> 2) & 3). With 288 rows there are 18 loads for 4 waves: each
+// wave issues 5, the two spare ones repeating a load (same bytes, same place).
+template <int ROWS>
 __device__ __forceinline__ Operand krows_operand(const uint16_t* rows, int valid_rows, int ld, int wave, int lane) {
+  constexpr int kInstr = ROWS / 16, kPer = (kInstr + 3) / 4;
   Operand op;
   op.base = rows;
   op.bytes = static_cast<uint32_t>(valid_rows) * static_cast<uint32_t>(ld) * 2u;
   op.stage_step = kBK * 2;
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    const int j = wave * 4 + jj;
+  for (int jj = 0; jj < kPer; ++jj) {
+    const int j = (wave * kPer + jj) % kInstr;
+    op.slot[jj] = j;
     const int r = 16 * j + (lane >> 2);
     const int c = (lane & 3) ^ ((lane >> 4) & 3);
     op.voff[jj] = static_cast<uint32_t>(r) * static_cast<uint32_t>(ld) * 2u + static_cast<uint32_t>(c) * 16u;
@@ -84,6 +91,7 @@ __device__ __forceinline__ Operand kmajor_operand(const uint16_t* krows, int val
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     const int j = wave * 4 + jj;
+    op.slot[jj] = j;
     const int kl = 2 * j + (lane >> 5);
     const int c = (lane & 31) ^ (4 * (kl & 3));
     op.voff[jj] = (static_cast<uint32_t>(kl) * static_cast<uint32_t>(ld) + static_cast<uint32_t>(col0 + 8 * c)) * 2u;
@@ -115,25 +123,43 @@ __device__ __forceinline__ uint32_t kmajor_read(int cb, int lane) {
 
 __device__ __forceinline__ float sigmoid_fast(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
+// mfma c += a * b with c held in VGPRs (the 256 accumulation registers are full)
+__device__ __forceinline__ void mfma_vgpr(f32x16_t& c, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+
 // up_off (kSwigluBwd): columns between gate and up halves of C and gu (= N).
-template <int MODE, int EPI>
+// XR (NT only): 1 for a 288-row tile, whose rows 256..287 every wave shares: each
+// wave multiplies them by two of its four column blocks. The second wave row keeps
+// its column blocks in swapped slots (block = slot ^ 2), so that both wave rows use
+// slots 0 and 1 for the extra rows and together cover all four blocks.
+template <int MODE, int EPI, int XR>
 __device__ __forceinline__ void bwd_tile(uint16_t* smem, const Operand& opa, const Operand& opb, int ksteps,
                                          uint16_t* __restrict__ C, int c_rows, int c_cols, int ldc,
                                          const uint16_t* __restrict__ gu, int up_off) {
+  static_assert(XR == 0 || MODE == kNT, "extra rows only in NT tiles");
+  constexpr int MX = XR ? 2 : 0;                                     // extra MFMA blocks per wave
+  constexpr int NA = XR ? 5 : 4;                                     // activation loads per wave per stage
+  constexpr int PER = NA + 4;                                        // DMA loads per wave per stage
+  constexpr int kAStage = MODE == kNT ? kNTAStageBytes : kOpStageBytes;
   const int lane = lane_id();
   const int wave = uniform(static_cast<int>(threadIdx.x) / kWave);
   const int wm = wave / 2, wn = wave % 2;
   const int l31 = lane & 31;
   const uint32_t sA = uniform(static_cast<int>(lds_addr(smem)));
-  const uint32_t sB = sA + kStages * kOpStageBytes;
+  const uint32_t sB = sA + kStages * kAStage;
+  // column block of B slot ni
+  auto blk = [&](int ni) { return XR && wm ? ni ^ 2 : ni; };
 
   // fragment read offsets
-  uint32_t a_rd[2], b_rd[2], at_rd[MI], bt_rd[NI];
+  uint32_t a_rd[2], a_rd_x[2], b_rd_lo[2], b_rd_hi[2], at_rd[MI], bt_rd[NI];
   if constexpr (MODE == kNT) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       a_rd[kk] = krows_read(wm * 128, kk, lane);
-      b_rd[kk] = krows_read(wn * 128, kk, lane);
+      a_rd_x[kk] = krows_read(256, kk, lane);
+      b_rd_lo[kk] = krows_read(wn * 128 + blk(0) * 32, kk, lane);  // slots 0, 1
+      b_rd_hi[kk] = krows_read(wn * 128 + blk(2) * 32, kk, lane);  // slots 2, 3
     }
   } else {
 #pragma unroll
@@ -141,24 +167,30 @@ __device__ __forceinline__ void bwd_tile(uint16_t* smem, const Operand& opa, con
 #pragma unroll
     for (int i = 0; i < NI; ++i) bt_rd[i] = kmajor_read(wn * 128 + i * 32, lane);
   }
-  // LDS reads of one 16-wide K slice: r < 4 the A blocks, then the B blocks (KROWS:
-  // one ds_read_b128 each; KMAJOR: two transposed reads each)
-  constexpr int R = MODE == kNT ? MI + NI : 2 * (MI + NI);
+  // LDS reads of one 16-wide K slice: the A blocks (and the extra row block), then
+  // the B blocks (KROWS: one ds_read_b128 each; KMAJOR: two transposed reads each)
+  constexpr int R = MODE == kNT ? MI + XR + NI : 2 * (MI + NI);
   auto read_one = [&](Frags<MODE>& f, int buf, auto kk_c, auto r_c) {
     constexpr int kk = decltype(kk_c)::value, r = decltype(r_c)::value;
     if constexpr (MODE == kNT) {
-      if constexpr (r < MI) f.a[r] = ds_read16<r * 2048>(sA + buf * kOpStageBytes + a_rd[kk]);
-      else f.b[r - MI] = ds_read16<(r - MI) * 2048>(sB + buf * kOpStageBytes + b_rd[kk]);
+      if constexpr (r < MI) {
+        f.a[r] = ds_read16<r * 2048>(sA + buf * kAStage + a_rd[kk]);
+      } else if constexpr (r < MI + XR) {
+        f.a[MI] = ds_read16<0>(sA + buf * kAStage + a_rd_x[kk]);
+      } else {
+        constexpr int ni = r - MI - XR;
+        f.b[ni] = ds_read16<(ni & 1) * 2048>(sB + buf * kOpStageBytes + (ni < 2 ? b_rd_lo[kk] : b_rd_hi[kk]));
+      }
     } else {
-      constexpr int blk = (r % (2 * MI)) / 2, h = r % 2;
-      if constexpr (r < 2 * MI) f.a[blk][h] = ds_read_tr<kk * 8192 + h * 2048>(sA + buf * kOpStageBytes + at_rd[blk]);
-      else f.b[blk][h] = ds_read_tr<kk * 8192 + h * 2048>(sB + buf * kOpStageBytes + bt_rd[blk]);
+      constexpr int blk_i = (r % (2 * MI)) / 2, h = r % 2;
+      if constexpr (r < 2 * MI) f.a[blk_i][h] = ds_read_tr<kk * 8192 + h * 2048>(sA + buf * kAStage + at_rd[blk_i]);
+      else f.b[blk_i][h] = ds_read_tr<kk * 8192 + h * 2048>(sB + buf * kOpStageBytes + bt_rd[blk_i]);
     }
   };
   auto tie_frags = [&](Frags<MODE>& f) {
     if constexpr (MODE == kNT) {
 #pragma unroll
-      for (int i = 0; i < MI; ++i) tie(f.a[i]);
+      for (int i = 0; i < MI + XR; ++i) tie(f.a[i]);
 #pragma unroll
       for (int i = 0; i < NI; ++i) tie(f.b[i]);
     } else {
@@ -182,48 +214,59 @@ __device__ __forceinline__ void bwd_tile(uint16_t* smem, const Operand& opa, con
     for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+  f32x16_t acc_x[MX > 0 ? MX : 1];
+#pragma unroll
+  for (int x = 0; x < MX; ++x)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc_x[x][r] = 0.f;
 
-  auto mfma_one = [&](const Frags<MODE>& f, auto q_c) {
-    constexpr int q = decltype(q_c)::value, mi = q / NI, ni = q % NI;
-    if constexpr (MODE == kNT)
-      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
-    else
-      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join(f.a[mi][0], f.a[mi][1]), join(f.b[ni][0], f.b[ni][1]),
-                                                            acc[mi][ni], 0, 0, 0);
+  // MFMA q of a slice: the extra row block first (its VGPR results are next read
+  // NM - MX MFMAs later, also after the last slice), then row-major over mi, ni
+  auto mfma_one = [&](const auto& f, auto q_c) {  // f: Frags<MODE> (a generic parameter, so
+    constexpr int q = decltype(q_c)::value;       // that the unused branch is not instantiated)
+    if constexpr (q < MX) {
+      mfma_vgpr(acc_x[q], f.a[MI], f.b[q]);
+    } else {
+      constexpr int mi = (q - MX) / NI, ni = (q - MX) % NI;
+      if constexpr (MODE == kNT)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
+      else
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join(f.a[mi][0], f.a[mi][1]),
+                                                              join(f.b[ni][0], f.b[ni][1]), acc[mi][ni], 0, 0, 0);
+    }
   };
 
-  // DMA of one stage: loads 0..3 the A operand, 4..7 the B operand (this wave's
-  // four 1 KB pieces of each)
+  // DMA of one stage: loads 0..NA-1 the A operand, then 4 of the B operand
   struct StageLoads {
     __amdgpu_buffer_rsrc_t ra, rb;
     uint32_t la, lb;
   };
   auto stage_loads = [&](int s) {
     const int buf = s % kStages;
-    return StageLoads{stage_rsrc(opa, s), stage_rsrc(opb, s), sA + buf * kOpStageBytes,
-                      sB + buf * kOpStageBytes};
+    return StageLoads{stage_rsrc(opa, s), stage_rsrc(opb, s), sA + buf * kAStage, sB + buf * kOpStageBytes};
   };
   auto dma_one = [&](const StageLoads& st, auto j_c) {
     constexpr int j = decltype(j_c)::value;
-    if constexpr (j < 4) dma16(st.ra, opa.voff[j], st.la + (wave * 4 + j) * 1024);
-    else dma16(st.rb, opb.voff[j - 4], st.lb + (wave * 4 + (j - 4)) * 1024);
+    if constexpr (j < NA) dma16(st.ra, opa.voff[j], st.la + opa.slot[j] * 1024);
+    else dma16(st.rb, opb.voff[j - NA], st.lb + opb.slot[j - NA] * 1024);
   };
   auto wait_stage = [&](int s) {
     const int after = min(kStages - 2, ksteps - 1 - s);
-    if (after >= 2) wait_vmcnt<2 * PER>();
-    else if (after == 1) wait_vmcnt<PER>();
-    else wait_vmcnt<0>();
+    static_for<0, kStages - 1>([&](auto a_c) {
+      constexpr int a = decltype(a_c)::value;
+      if (after == a) wait_vmcnt<a * PER>();
+    });
   };
   using K0 = std::integral_constant<int, 0>;
   using K1 = std::integral_constant<int, 1>;
-  constexpr int NM = MI * NI;
+  constexpr int NM = MI * NI + MX;
   // reads per MFMA: all of a slice's reads go out in the first three quarters of
   // the slice, so the last has a quarter slice of MFMAs to land
   constexpr int RPM = (R + (NM * 3 / 4) - 1) / (NM * 3 / 4);
 
-  // One stage, as in the forward kernel: slice 0 carries slice 1's reads, one per
-  // MFMA; the stage barrier; slice 1 carries the next stage's slice-0 reads, one
-  // per MFMA, and the DMA of stage ks + kStages, one per two MFMAs.
+  // One stage, as in the forward kernel: slice 0 carries slice 1's reads; the
+  // stage barrier; slice 1 carries the next stage's slice-0 reads and the DMA of
+  // stage ks + kStages, one load per two MFMAs.
   Frags<MODE> f0, f1;
   auto stage = [&](int ks, auto dma_c, auto more_c) {
     constexpr bool DMA = decltype(dma_c)::value, MORE = decltype(more_c)::value;
@@ -259,6 +302,7 @@ __device__ __forceinline__ void bwd_tile(uint16_t* smem, const Operand& opa, con
       if constexpr (DMA && q % 2 == 0 && q / 2 < PER) dma_one(st, std::integral_constant<int, q / 2>{});
       __builtin_amdgcn_sched_barrier(0);
     });
+    if constexpr (DMA) static_for<((NM + 1) / 2 < PER ? (NM + 1) / 2 : PER), PER>([&](auto j) { dma_one(st, j); });
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -283,47 +327,48 @@ __device__ __forceinline__ void bwd_tile(uint16_t* smem, const Operand& opa, con
   // ---- epilogue: C is c_rows x c_cols (row stride ldc) at the tile origin --------
   const __amdgpu_buffer_rsrc_t rc =
       make_rsrc(C, static_cast<uint32_t>(c_rows) * static_cast<uint32_t>(ldc) * 2u);
-#pragma unroll
-  for (int ni = 0; ni < NI; ++ni) {
-    const int col = wn * 128 + ni * 32 + l31;
+  // one 32 x 32 block whose rows start at row_base and whose lane column is col
+  auto store_block = [&](const f32x16_t& a, int row_base, int col) {
     const uint32_t coff = col < c_cols ? static_cast<uint32_t>(col) * 2u : 0x80000000u;
+    if constexpr (EPI == kSwigluBwd) {
+      // a = dH at (row, f = col); G and U of the same element from gu [rows][2 N]
+      // (ldc = 2 N); dG goes to column f and dU to column N + f of C
+      const __amdgpu_buffer_rsrc_t rg = make_rsrc(gu, static_cast<uint32_t>(c_rows) * static_cast<uint32_t>(ldc) * 2u);
+      const uint32_t uoff = col < c_cols ? static_cast<uint32_t>(up_off + col) * 2u : 0x80000000u;
+      float g[16], u[16];
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      if constexpr (EPI == kSwigluBwd) {
-        // acc = dH at (row, f = col); G and U of the same element from gu [rows][2 N]
-        // (ldc = 2 N); dG goes to column f and dU to column N + f of C
-        const __amdgpu_buffer_rsrc_t rg = make_rsrc(gu, static_cast<uint32_t>(c_rows) * static_cast<uint32_t>(ldc) * 2u);
-        const uint32_t uoff = col < c_cols ? static_cast<uint32_t>(up_off + col) * 2u : 0x80000000u;
-        float g[16], u[16];
+      for (int r = 0; r < 16; ++r) {
+        const int row = row_base + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const uint32_t ro = static_cast<uint32_t>(row) * static_cast<uint32_t>(ldc) * 2u;
+        g[r] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rg, static_cast<int>(ro + coff), 0, 0));
+        u[r] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rg, static_cast<int>(ro + uoff), 0, 0));
+      }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = wm * 128 + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          const uint32_t ro = static_cast<uint32_t>(row) * static_cast<uint32_t>(ldc) * 2u;
-          g[r] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rg, static_cast<int>(ro + coff), 0, 0));
-          u[r] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rg, static_cast<int>(ro + uoff), 0, 0));
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int row = row_base + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const uint32_t ro = static_cast<uint32_t>(row) * static_cast<uint32_t>(ldc) * 2u;
+        const float dh = a[r];
+        const float s = sigmoid_fast(g[r]);
+        const float dg = dh * u[r] * (s * (1.0f + g[r] * (1.0f - s)));
+        const float du = dh * g[r] * s;
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(dg), rc, static_cast<int>(ro + coff), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(du), rc, static_cast<int>(ro + uoff), 0, 0);
+      }
+    } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = wm * 128 + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          const uint32_t ro = static_cast<uint32_t>(row) * static_cast<uint32_t>(ldc) * 2u;
-          const float dh = acc[mi][ni][r];
-          const float s = sigmoid_fast(g[r]);
-          const float dg = dh * u[r] * (s * (1.0f + g[r] * (1.0f - s)));
-          const float du = dh * g[r] * s;
-          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(dg), rc, static_cast<int>(ro + coff), 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(du), rc, static_cast<int>(ro + uoff), 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = wm * 128 + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          const uint32_t ro = static_cast<uint32_t>(row) * static_cast<uint32_t>(ldc) * 2u;
-          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(acc[mi][ni][r]), rc, static_cast<int>(ro + coff), 0,
-                                                0);
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int row = row_base + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const uint32_t ro = static_cast<uint32_t>(row) * static_cast<uint32_t>(ldc) * 2u;
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(a[r]), rc, static_cast<int>(ro + coff), 0, 0);
       }
     }
-  }
+  };
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) store_block(acc[mi][ni], wm * 128 + mi * 32, wn * 128 + blk(ni) * 32 + l31);
+#pragma unroll
+  for (int x = 0; x < MX; ++x) store_block(acc_x[x], 256, wn * 128 + blk(x) * 32 + l31);
 }
 
 // NT: C[rows, N] = A[rows, K] @ B_e[N, K]^T over row tiles of each local expert.
@@ -334,9 +379,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_nt_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
     const uint16_t* __restrict__ gu, const int32_t* __restrict__ offsets, int e_begin, int e_loc, int K, int N,
     int ldc, int n_max) {
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[kStages * 2 * 256 * kBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[kStages * (288 + 256) * kBK];
   __shared__ TileMap tm;
-  build_tile_map<256>(tm, offsets, e_begin, e_loc, n_max);
+  // a remainder of at most 32 rows rides on the expert's last full tile (288 rows)
+  build_tile_map<256, 32>(tm, offsets, e_begin, e_loc, n_max);
   const int n_tiles = (N + 255) / 256;
   const int total = uniform(tm.mstart[e_loc]) * n_tiles;
   const int lane = lane_id();
@@ -344,13 +390,20 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_nt_kernel(
   for (int tile = xcd_remap(blockIdx.x, gridDim.x); tile < total; tile += gridDim.x) {
     const TileCoord tc = find_tile(tm, tile, n_tiles, e_loc);
     const int row0 = uniform(tm.rstart[tc.e]) + tc.mt * 256;
-    const int rows = min(256, uniform(tm.rstart[tc.e + 1]) - row0);
+    const int mt_e = uniform(tm.mstart[tc.e + 1]) - uniform(tm.mstart[tc.e]);
+    const int rows = tc.mt == mt_e - 1 ? uniform(tm.rstart[tc.e + 1]) - row0 : 256;
     const int n0 = tc.nt * 256;
     const uint16_t* Bexp = B + static_cast<int64_t>(tc.e) * N * K;
-    const Operand opa = krows_operand(A + static_cast<int64_t>(row0) * K, rows, K, wave, lane);
-    const Operand opb = krows_operand(Bexp + static_cast<int64_t>(n0) * K, N - n0, K, wave, lane);
-    bwd_tile<kNT, EPI>(smem, opa, opb, K / kBK, C + static_cast<int64_t>(row0) * ldc + n0, rows, N - n0, ldc,
-                       EPI == kSwigluBwd ? gu + static_cast<int64_t>(row0) * ldc + n0 : nullptr, N);
+    const Operand opb = krows_operand<256>(Bexp + static_cast<int64_t>(n0) * K, N - n0, K, wave, lane);
+    uint16_t* Ct = C + static_cast<int64_t>(row0) * ldc + n0;
+    const uint16_t* gut = EPI == kSwigluBwd ? gu + static_cast<int64_t>(row0) * ldc + n0 : nullptr;
+    if (rows > 256) {
+      const Operand opa = krows_operand<288>(A + static_cast<int64_t>(row0) * K, rows, K, wave, lane);
+      bwd_tile<kNT, EPI, 1>(smem, opa, opb, K / kBK, Ct, rows, N - n0, ldc, gut, N);
+    } else {
+      const Operand opa = krows_operand<256>(A + static_cast<int64_t>(row0) * K, rows, K, wave, lane);
+      bwd_tile<kNT, EPI, 0>(smem, opa, opb, K / kBK, Ct, rows, N - n0, ldc, gut, N);
+    }
     __builtin_amdgcn_s_barrier();
   }
 }
@@ -376,7 +429,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_tn_kernel(
     const int m0 = mt * 256, n0 = nt * 256;
     const Operand opa = kmajor_operand(src_a + static_cast<int64_t>(r0) * M, rows, M, m0, wave, lane);
     const Operand opb = kmajor_operand(src_b + static_cast<int64_t>(r0) * N, rows, N, n0, wave, lane);
-    bwd_tile<kTN, kPlain>(smem, opa, opb, (rows + kBK - 1) / kBK,
+    bwd_tile<kTN, kPlain, 0>(smem, opa, opb, (rows + kBK - 1) / kBK,
                           dW + static_cast<int64_t>(e) * M * N + static_cast<int64_t>(m0) * N + n0, M - m0, N - n0, N,
                           nullptr, 0);
     __builtin_amdgcn_s_barrier();
