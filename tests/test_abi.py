@@ -112,8 +112,11 @@ def test_workspace_sizes():
     s = _shape(T=0)
     assert lib.moe_dispatch_workspace_bytes(ctypes.byref(s)) == 0
     s = _shape(T=16384, k=8, E=256)
-    # per (expert, chunk of 1024 pairs): the histogram and the chunk bases; plus E totals
-    assert lib.moe_dispatch_workspace_bytes(ctypes.byref(s)) == (2 * 256 * 128 + 256) * 4
+    # per (expert, chunk of 256 pairs): the histogram and the chunk bases; plus E totals
+    assert lib.moe_dispatch_workspace_bytes(ctypes.byref(s)) == (2 * 256 * 512 + 256) * 4
+    # chunks of 1024 pairs once the tables would pass 4M entries
+    s = _shape(T=2**20, k=8, E=1024)
+    assert lib.moe_dispatch_workspace_bytes(ctypes.byref(s)) == (2 * 1024 * 8192 + 1024) * 4
     assert lib.moe_grouped_gemm_workspace_bytes(ctypes.byref(s), moe.MOE_BF16) == 0
 
 

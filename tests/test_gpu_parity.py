@@ -334,3 +334,26 @@ def test_decode_shaped_skewed_layer_matches_oracle(w):
                       g.to_dev(wdn, w.dtype), w.k, w.e_begin, w.e_end, fused=True)
     torch.cuda.synchronize()
     assert torch.equal(fused["out"], res["out"])
+
+
+@pytest.mark.parametrize("T,k,E,lo,hi", [(600000, 8, 256, 0, 32), (4096, 8, 256, 0, 32), (70000, 4, 128, 16, 32)],
+                         ids=["chunks_of_1024", "chunks_of_256", "chunks_of_256_ragged"])
+def test_dispatch_both_chunk_sizes(T, k, E, lo, hi):
+    """The dispatch switches from 256-pair to 1024-pair chunks once its (expert,
+    chunk) tables would pass 4M entries; both give the stable permutation."""
+    rng = np.random.default_rng(T + k + E)
+    idx_np = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    x = torch.empty((T, 8), dtype=torch.bfloat16, device="cuda")
+    disp = moe.dispatch(x, torch.from_numpy(idx_np).cuda(), E, lo, hi, gather=False)
+    torch.cuda.synchronize()
+    flat = idx_np.reshape(-1)
+    counts = np.bincount(flat, minlength=E)
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    perm = np.argsort(flat, kind="stable")
+    np.testing.assert_array_equal(disp.counts.cpu().numpy(), counts)
+    np.testing.assert_array_equal(disp.offsets.cpu().numpy(), offsets)
+    np.testing.assert_array_equal(disp.perm.cpu().numpy(), perm)
+    seg0, seg1 = offsets[lo], offsets[hi]
+    pair_pos = np.full(T * k, -1)
+    pair_pos[perm[seg0:seg1]] = np.arange(seg1 - seg0)
+    np.testing.assert_array_equal(disp.pair_pos.cpu().numpy(), pair_pos)

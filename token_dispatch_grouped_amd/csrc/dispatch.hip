@@ -8,7 +8,7 @@
 // pairs are one contiguous segment of the expert-sorted pair list).
 //
 // Design (five small launches, all bounded by the pair count or HBM):
-//   1. count   : one workgroup per chunk of kDispatchChunk flat pairs builds an
+//   1. count   : one workgroup per chunk of 256 (or 1024) flat pairs builds an
 //                LDS histogram and stores it expert-major: ws[e * n_chunks + c].
 //   2. scan    : two launches with one wave per expert: per-expert totals,
 //                then counts, offsets and the first sorted slot of chunk c's
@@ -28,14 +28,15 @@ namespace {
 
 constexpr int kThreads = 256;
 
+template <int CHUNK>
 __global__ __launch_bounds__(kThreads) void dispatch_count_kernel(const int32_t* __restrict__ idx,
                                                                   int32_t* __restrict__ ws,
                                                                   int64_t P, int E, int n_chunks) {
   __shared__ int hist[kMaxExperts];
   for (int e = threadIdx.x; e < E; e += kThreads) hist[e] = 0;
   __syncthreads();
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * kDispatchChunk;
-  for (int i = threadIdx.x; i < kDispatchChunk; i += kThreads) {
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * CHUNK;
+  for (int i = threadIdx.x; i < CHUNK; i += kThreads) {
     const int64_t p = base + i;
     if (p < P) {
       const int e = idx[p];
@@ -132,12 +133,13 @@ __global__ __launch_bounds__(kThreads) void dispatch_bases_kernel(const int32_t*
   }
 }
 
+template <int CHUNK>
 __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ base,
     const int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
     int32_t* __restrict__ pair_pos, int64_t P, int E, int e_begin, int e_end) {
   constexpr int kWaves = kThreads / kWave;
-  constexpr int kPasses = kDispatchChunk / kThreads;
+  constexpr int kPasses = CHUNK / kThreads;
   __shared__ int run[kMaxExperts];            // next sorted slot of each expert for this chunk
   __shared__ int wcnt[kWaves][kMaxExperts];   // per-wave counts of the current pass
   const int tid = threadIdx.x;
@@ -150,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
   int ids[kPasses];
 #pragma unroll
   for (int pass = 0; pass < kPasses; ++pass) {
-    const int64_t p = static_cast<int64_t>(chunk) * kDispatchChunk + pass * kThreads + tid;
+    const int64_t p = static_cast<int64_t>(chunk) * CHUNK + pass * kThreads + tid;
     ids[pass] = p < P ? idx[p] : -1;
   }
   const int32_t* brow = base + static_cast<int64_t>(chunk) * E;
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
   for (int pass = 0; pass < kPasses; ++pass) {
     for (int i = tid; i < kWaves * E; i += kThreads) wcnt[i / E][i % E] = 0;
     __syncthreads();
-    const int64_t p = static_cast<int64_t>(chunk) * kDispatchChunk + pass * kThreads + tid;
+    const int64_t p = static_cast<int64_t>(chunk) * CHUNK + pass * kThreads + tid;
     const int e = ids[pass];
     const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(E);
     if (p < P && !valid) pair_pos[p] = -1;
@@ -169,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
     uint64_t peers = 0;
     while (remaining) {
       const int leader = __ffsll(static_cast<unsigned long long>(remaining)) - 1;
-      const int le = __shfl(e, leader);
+      const int le = __builtin_amdgcn_readlane(e, leader);  // leader is wave-uniform
       const uint64_t m = __ballot(valid && e == le);
       if (valid && e == le) peers = m;
       remaining &= ~m;
@@ -228,9 +230,17 @@ __global__ __launch_bounds__(kThreads) void dispatch_gather_kernel(
 
 }  // namespace
 
+// Pairs per chunk: 256 (one pass of a workgroup, and four times the workgroups of
+// 1024-pair chunks), unless the (expert, chunk) tables would pass 4M entries.
+int dispatch_chunk(int64_t P, int E) {
+  const int64_t n256 = (P + 255) / 256;
+  return n256 * E <= (int64_t{1} << 22) ? 256 : 1024;
+}
+
 size_t dispatch_workspace_bytes(int64_t T, int k, int E) {
   const int64_t P = T * k;
-  const int64_t n_chunks = (P + kDispatchChunk - 1) / kDispatchChunk;
+  const int chunk = dispatch_chunk(P, E);
+  const int64_t n_chunks = (P + chunk - 1) / chunk;
   if (n_chunks == 0) return 0;
   // per-(expert, chunk) counts, per-(chunk, expert) first slots, per-expert totals
   return (2 * static_cast<size_t>(n_chunks * E) + E) * sizeof(int32_t);
@@ -241,11 +251,16 @@ hipError_t launch_dispatch(const void* x, size_t row_bytes, const int32_t* idx, 
                            void* workspace, int64_t T, int k, int E, int e_begin, int e_end,
                            int64_t n_max, hipStream_t stream) {
   const int64_t P = T * k;
-  const int n_chunks = static_cast<int>((P + kDispatchChunk - 1) / kDispatchChunk);
+  const int chunk = dispatch_chunk(P, E);
+  const int n_chunks = static_cast<int>((P + chunk - 1) / chunk);
   int32_t* ws = static_cast<int32_t*>(workspace);
   if (n_chunks > 0) {
-    hipLaunchKernelGGL(dispatch_count_kernel, dim3(n_chunks), dim3(kThreads), 0, stream, idx, ws, P,
-                       E, n_chunks);
+    if (chunk == 256)
+      hipLaunchKernelGGL(dispatch_count_kernel<256>, dim3(n_chunks), dim3(kThreads), 0, stream, idx, ws, P, E,
+                         n_chunks);
+    else
+      hipLaunchKernelGGL(dispatch_count_kernel<1024>, dim3(n_chunks), dim3(kThreads), 0, stream, idx, ws, P, E,
+                         n_chunks);
   }
   int32_t* bases = ws + static_cast<int64_t>(n_chunks) * E;
   int32_t* tot = bases + static_cast<int64_t>(n_chunks) * E;
@@ -258,8 +273,12 @@ hipError_t launch_dispatch(const void* x, size_t row_bytes, const int32_t* idx, 
   hipLaunchKernelGGL(dispatch_totals_kernel, dim3(scan_blocks), dim3(kThreads), 0, stream, ws, tot, E, n_chunks);
   hipLaunchKernelGGL(dispatch_bases_kernel, dim3(scan_blocks), dim3(kThreads), 0, stream, ws, tot, bases, counts,
                      offsets, E, n_chunks);
-  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(n_chunks), dim3(kThreads), 0, stream, idx, bases,
-                     offsets, perm, pair_pos, P, E, e_begin, e_end);
+  if (chunk == 256)
+    hipLaunchKernelGGL(dispatch_scatter_kernel<256>, dim3(n_chunks), dim3(kThreads), 0, stream, idx, bases, offsets,
+                       perm, pair_pos, P, E, e_begin, e_end);
+  else
+    hipLaunchKernelGGL(dispatch_scatter_kernel<1024>, dim3(n_chunks), dim3(kThreads), 0, stream, idx, bases, offsets,
+                       perm, pair_pos, P, E, e_begin, e_end);
   if (x_perm == nullptr) return hipGetLastError();  // indices only: the rows are gathered by the GEMM
   return launch_gather_rows(x, row_bytes, perm, offsets, x_perm, k, e_begin, e_end, n_max, stream);
 }

@@ -12,9 +12,6 @@ namespace moe {
 constexpr int kWave = 64;
 constexpr int kMaxExperts = 1024;
 
-// Pairs handled by one dispatch workgroup (256 threads x 4 passes).
-constexpr int kDispatchChunk = 1024;
-
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
