@@ -94,6 +94,113 @@ __device__ __forceinline__ int xcd_remap(int b, int G) {
   return (G & 7) == 0 ? (b & 7) * (G >> 3) + (b >> 3) : b;
 }
 
+// Tile map with the experts ordered by the height of their tiles, largest first:
+// class 0 = more than 128 rows (tiles of 256 or 288 rows), then (64, 128],
+// (32, 64], (0, 32], empty last; stable by expert id inside a class. Walked in
+// snake order (see snake_tile), the costly tiles start in the first round and
+// the second round's cheap tiles go to the workgroups whose first tiles were
+// cheap. When every expert is in one class the order is the plain expert order.
+struct SortedTileMap {
+  int mstart[kMaxExperts + 1];  // row-tile prefix over positions
+  int eid[kMaxExperts];         // local expert at each position
+  int rstart[kMaxExperts + 1];  // first row of each expert (by expert id), relative to the local segment
+};
+
+__device__ __forceinline__ int height_class(int rows) {
+  return rows > 128 ? 0 : rows > 64 ? 1 : rows > 32 ? 2 : rows > 0 ? 3 : 4;
+}
+
+template <int BM, int MERGE_TAIL>
+__device__ void build_sorted_tile_map(SortedTileMap& tm, const int32_t* __restrict__ offsets, int e_begin,
+                                      int e_loc, int n_max) {
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    const int base = offsets[e_begin];
+    auto rows_of = [&](int e) {
+      const int start = min(offsets[e_begin + e] - base, n_max);
+      return min(offsets[e_begin + e + 1] - base, n_max) - start;
+    };
+    // pass 1: experts per class, and the row starts
+    int cnt[5] = {0, 0, 0, 0, 0};
+    for (int e0 = 0; e0 < e_loc; e0 += kWave) {
+      const int e = e0 + lane;
+      const int c = e < e_loc ? height_class(rows_of(e)) : 5;
+      if (e < e_loc) tm.rstart[e] = min(offsets[e_begin + e] - base, n_max);
+#pragma unroll
+      for (int q = 0; q < 5; ++q) cnt[q] += __popcll(__ballot(c == q));
+    }
+    if (lane == 0) tm.rstart[e_loc] = min(offsets[e_begin + e_loc] - base, n_max);
+    int cbase[5];
+    cbase[0] = 0;
+#pragma unroll
+    for (int q = 1; q < 5; ++q) cbase[q] = cbase[q - 1] + cnt[q - 1];
+    // pass 2: position = class base + rank inside the class; row tiles parked in mstart
+    const uint64_t below = (uint64_t{1} << lane) - 1;
+    for (int e0 = 0; e0 < e_loc; e0 += kWave) {
+      const int e = e0 + lane;
+      const int rows = e < e_loc ? rows_of(e) : 0;
+      const int c = e < e_loc ? height_class(rows) : 5;
+      int pos = 0;
+#pragma unroll
+      for (int q = 0; q < 5; ++q) {
+        const uint64_t m = __ballot(c == q);
+        if (c == q) pos = cbase[q] + __popcll(m & below);
+        cbase[q] += __popcll(m);
+      }
+      if (e < e_loc) {
+        tm.eid[pos] = e;
+        tm.mstart[pos] = row_tiles<BM, MERGE_TAIL>(rows);
+      }
+    }
+    // pass 3: exclusive prefix of the row tiles over positions (a position may
+    // have been written by another lane: the fences keep the reads after the writes)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    int carry = 0;
+    for (int p0 = 0; p0 < e_loc; p0 += kWave) {
+      const int p = p0 + lane;
+      const int mt = p < e_loc ? tm.mstart[p] : 0;
+      int incl = mt;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      if (p < e_loc) tm.mstart[p] = carry + incl - mt;
+      carry += __shfl(incl, kWave - 1);
+    }
+    if (lane == 0) tm.mstart[e_loc] = carry;
+  }
+  __syncthreads();
+}
+
+struct SortedTile {
+  int e, mt, nt, mt_e;
+};
+
+// Position p with mstart[p]*n_tiles <= tile < mstart[p+1]*n_tiles; empty experts
+// own no ids. Row tile fastest inside a column block, as in find_tile.
+__device__ __forceinline__ SortedTile find_sorted_tile(const SortedTileMap& tm, int tile, int n_tiles, int e_loc) {
+  int lo = 0, hi = e_loc;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (tm.mstart[mid] * n_tiles <= tile) lo = mid;
+    else hi = mid;
+  }
+  lo = uniform(lo);
+  const int ms = uniform(tm.mstart[lo]);
+  const int mt_e = uniform(tm.mstart[lo + 1]) - ms;
+  const int local = tile - ms * n_tiles;
+  return {uniform(tm.eid[lo]), local % mt_e, local / mt_e, mt_e};
+}
+
+// Tile of round i for a workgroup whose XCD-remapped index is r: rounds go
+// forward and backward in turn over the tile ids.
+__device__ __forceinline__ int snake_tile(int i, int r, int G) {
+  return (i & 1) ? (i + 1) * G - 1 - r : i * G + r;
+}
+
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 

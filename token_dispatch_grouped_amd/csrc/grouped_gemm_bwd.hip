@@ -380,18 +380,20 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_nt_kernel(
     const uint16_t* __restrict__ gu, const int32_t* __restrict__ offsets, int e_begin, int e_loc, int K, int N,
     int ldc, int n_max) {
   __shared__ __attribute__((aligned(1024))) uint16_t smem[kStages * (288 + 256) * kBK];
-  __shared__ TileMap tm;
+  __shared__ SortedTileMap tm;
   // a remainder of at most 32 rows rides on the expert's last full tile (288 rows)
-  build_tile_map<256, 32>(tm, offsets, e_begin, e_loc, n_max);
+  build_sorted_tile_map<256, 32>(tm, offsets, e_begin, e_loc, n_max);
   const int n_tiles = (N + 255) / 256;
   const int total = uniform(tm.mstart[e_loc]) * n_tiles;
   const int lane = lane_id();
   const int wave = uniform(static_cast<int>(threadIdx.x) / kWave);
-  for (int tile = xcd_remap(blockIdx.x, gridDim.x); tile < total; tile += gridDim.x) {
-    const TileCoord tc = find_tile(tm, tile, n_tiles, e_loc);
+  const int G = gridDim.x, r = xcd_remap(blockIdx.x, G);
+  for (int i = 0;; ++i) {
+    const int tile = snake_tile(i, r, G);
+    if (tile >= total) break;  // later rounds hold only larger ids
+    const SortedTile tc = find_sorted_tile(tm, tile, n_tiles, e_loc);
     const int row0 = uniform(tm.rstart[tc.e]) + tc.mt * 256;
-    const int mt_e = uniform(tm.mstart[tc.e + 1]) - uniform(tm.mstart[tc.e]);
-    const int rows = tc.mt == mt_e - 1 ? uniform(tm.rstart[tc.e + 1]) - row0 : 256;
+    const int rows = tc.mt == tc.mt_e - 1 ? uniform(tm.rstart[tc.e + 1]) - row0 : 256;
     const int n0 = tc.nt * 256;
     const uint16_t* Bexp = B + static_cast<int64_t>(tc.e) * N * K;
     const Operand opb = krows_operand<256>(Bexp + static_cast<int64_t>(n0) * K, N - n0, K, wave, lane);

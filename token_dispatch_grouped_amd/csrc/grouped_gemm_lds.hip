@@ -376,9 +376,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_lds_kernel(
     const int32_t* __restrict__ offsets, int e_begin, int e_loc, int K, int N, int ldb, int n_max,
     const int32_t* __restrict__ perm, int k, uint32_t a_bytes) {
   __shared__ __attribute__((aligned(1024))) uint16_t smem[kStages * (kAStageElems + kBStageElems)];
-  __shared__ TileMap tm;
+  __shared__ SortedTileMap tm;
   // a remainder of at most 32 rows rides on the expert's last full tile (288 rows)
-  build_tile_map<256, 32>(tm, offsets, e_begin, e_loc, n_max);
+  build_sorted_tile_map<256, 32>(tm, offsets, e_begin, e_loc, n_max);
 
   constexpr int kOutCols = SWIGLU ? 128 : 256;
   const int n_tiles = (N + kOutCols - 1) / kOutCols;
@@ -387,12 +387,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_lds_kernel(
   ARows ar{nullptr, k, a_bytes};
   if (GATHER) ar.perm_seg = perm + offsets[e_begin];
 
-  for (int tile = xcd_remap(blockIdx.x, gridDim.x); tile < total; tile += gridDim.x) {
-    const TileCoord tc = find_tile(tm, tile, n_tiles, e_loc);
+  const int G = gridDim.x, r = xcd_remap(blockIdx.x, G);
+  for (int i = 0;; ++i) {
+    const int tile = snake_tile(i, r, G);
+    if (tile >= total) break;  // later rounds hold only larger ids
+    const SortedTile tc = find_sorted_tile(tm, tile, n_tiles, e_loc);
     const int row0 = uniform(tm.rstart[tc.e]) + tc.mt * 256;
     const int row_end = uniform(tm.rstart[tc.e + 1]);
-    const int mt_e = uniform(tm.mstart[tc.e + 1]) - uniform(tm.mstart[tc.e]);
-    const int rows_valid = tc.mt == mt_e - 1 ? row_end - row0 : 256;
+    const int rows_valid = tc.mt == tc.mt_e - 1 ? row_end - row0 : 256;
     const int n0 = tc.nt * kOutCols;
     const uint16_t* Bexp = B + static_cast<int64_t>(tc.e) * b_expert;
     if (rows_valid > 256)
