@@ -91,7 +91,10 @@ def test_route_topk_ties_and_signed_zeros(E, k):
 
 @pytest.mark.parametrize("T,E,k,lo,hi", [(1, 8, 2, 0, 8), (1000, 8, 2, 0, 8), (1500, 32, 4, 8, 12),
                                          (3000, 256, 8, 0, 32), (2047, 1024, 4, 1000, 1024),
-                                         (5, 128, 4, 0, 128), (1025, 16, 16, 3, 4)])
+                                         (5, 128, 4, 0, 128), (1025, 16, 16, 3, 4),
+                                         # either side of the single-workgroup path (at most 2048 pairs)
+                                         (2047, 8, 1, 0, 8), (1024, 1024, 2, 512, 1024), (683, 128, 3, 16, 32),
+                                         (1, 1024, 1024, 0, 1024), (256, 256, 8, 0, 32)])
 def test_dispatch_matches_oracle(T, E, k, lo, hi):
     rng = np.random.default_rng(T + E + k)
     logits = rng.standard_normal((T, E)).astype(np.float32)

@@ -7,7 +7,8 @@
 // tamanhos se combinam" (a rank owns one contiguous block of experts, so its
 // pairs are one contiguous segment of the expert-sorted pair list).
 //
-// Design (five small launches, all bounded by the pair count or HBM):
+// Design (five small launches, all bounded by the pair count or HBM; a batch of
+// at most 2048 pairs takes one single-workgroup launch instead of 1-3):
 //   1. count   : one workgroup per chunk of 256 (or 1024) flat pairs builds an
 //                LDS histogram and stores it expert-major: ws[e * n_chunks + c].
 //   2. scan    : two launches with one wave per expert: per-expert totals,
@@ -195,6 +196,98 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
   }
 }
 
+// Up to kSmallPairs pairs: the whole dispatch in one workgroup of 1024 threads
+// (histogram, scan and the same stable scatter, one pass per 1024 pairs), so a
+// decode-sized batch pays one launch instead of four.
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallPairs = 2048;
+
+__global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(
+    const int32_t* __restrict__ idx, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm, int32_t* __restrict__ pair_pos, int P, int E, int e_begin, int e_end) {
+  constexpr int kWaves = kSmallThreads / kWave;
+  constexpr int kPasses = kSmallPairs / kSmallThreads;
+  __shared__ int run[kMaxExperts + 1];        // histogram, then the next sorted slot of each expert
+  __shared__ int wcnt[kWaves][kMaxExperts];   // per-wave counts of the current pass
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wv = tid / kWave;
+  const uint64_t lt_mask = (uint64_t{1} << lane) - 1;
+  int ids[kPasses];
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int p = pass * kSmallThreads + tid;
+    ids[pass] = p < P ? idx[p] : -1;
+  }
+  for (int e = tid; e < E; e += kSmallThreads) run[e] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass)
+    if (static_cast<unsigned>(ids[pass]) < static_cast<unsigned>(E)) atomicAdd(&run[ids[pass]], 1);
+  __syncthreads();
+  if (wv == 0) {  // exclusive scan: counts, offsets, and each expert's first slot
+    int carry = 0;
+    for (int e0 = 0; e0 < E; e0 += kWave) {
+      const int e = e0 + lane;
+      const int v = e < E ? run[e] : 0;
+      int incl = v;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      if (e < E) {
+        counts[e] = v;
+        offsets[e] = carry + incl - v;
+        run[e] = carry + incl - v;
+      }
+      carry += __shfl(incl, kWave - 1);
+    }
+    if (lane == 0) {
+      offsets[E] = carry;
+      run[E] = carry;
+    }
+  }
+  __syncthreads();
+  const int seg0 = run[e_begin];  // the first local slot (read before any pass moves run)
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    if (pass * kSmallThreads >= P) break;  // uniform
+    for (int i = tid; i < kWaves * E; i += kSmallThreads) wcnt[i / E][i % E] = 0;
+    __syncthreads();
+    const int p = pass * kSmallThreads + tid;
+    const int e = ids[pass];
+    const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(E);
+    if (p < P && !valid) pair_pos[p] = -1;
+    uint64_t remaining = __ballot(valid);
+    uint64_t peers = 0;
+    while (remaining) {
+      const int leader = __ffsll(static_cast<unsigned long long>(remaining)) - 1;
+      const int le = __builtin_amdgcn_readlane(e, leader);
+      const uint64_t m = __ballot(valid && e == le);
+      if (valid && e == le) peers = m;
+      remaining &= ~m;
+    }
+    const int rank = __popcll(peers & lt_mask);
+    if (valid && rank == 0) wcnt[wv][e] = __popcll(peers);
+    __syncthreads();
+    if (valid) {
+      int pos = run[e] + rank;
+      for (int w2 = 0; w2 < wv; ++w2) pos += wcnt[w2][e];
+      perm[pos] = p;
+      pair_pos[p] = (e >= e_begin && e < e_end) ? pos - seg0 : -1;
+    }
+    __syncthreads();
+    for (int x = tid; x < E; x += kSmallThreads) {
+      int add = 0;
+      for (int w2 = 0; w2 < kWaves; ++w2) add += wcnt[w2][x];
+      run[x] += add;
+    }
+    __syncthreads();
+  }
+}
+
 // Rows are copied in parts of kGatherVec 16-byte vectors (8 per lane), one part
 // per wave, so that a few long rows still spread over many waves and every lane
 // keeps 8 loads in flight.
@@ -251,6 +344,12 @@ hipError_t launch_dispatch(const void* x, size_t row_bytes, const int32_t* idx, 
                            void* workspace, int64_t T, int k, int E, int e_begin, int e_end,
                            int64_t n_max, hipStream_t stream) {
   const int64_t P = T * k;
+  if (P > 0 && P <= kSmallPairs) {
+    hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(kSmallThreads), 0, stream, idx, counts, offsets, perm,
+                       pair_pos, static_cast<int>(P), E, e_begin, e_end);
+    if (x_perm == nullptr) return hipGetLastError();
+    return launch_gather_rows(x, row_bytes, perm, offsets, x_perm, k, e_begin, e_end, n_max, stream);
+  }
   const int chunk = dispatch_chunk(P, E);
   const int n_chunks = static_cast<int>((P + chunk - 1) / chunk);
   int32_t* ws = static_cast<int32_t*>(workspace);

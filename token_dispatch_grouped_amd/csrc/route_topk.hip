@@ -9,9 +9,10 @@
 // VPL logits in registers, expert e = g + v*G, so a group's loads are contiguous.
 // A logit and its id form one 64-bit key (order-preserving float bits << 32 |
 // ~id), so "larger value, then lower id" is a plain unsigned max and every key
-// is unique. Each of the k rounds is a register max plus a group maximum
-// (DPP moves inside each 16-lane row, readlane across rows); the owning lane
-// then retires its key. HBM-bound: T*E*4 bytes read.
+// is unique. Each lane sorts its keys once (a bitonic network in registers);
+// each of the k rounds is then a group maximum of the lanes' largest keys (DPP
+// moves inside each 16-lane row, readlane across rows), and the owning lane
+// drops its largest key. HBM-bound: T*E*4 bytes read.
 #include "moe_internal.h"
 
 namespace moe {
@@ -67,53 +68,97 @@ __device__ __forceinline__ uint64_t group_max(uint64_t v) {
   return v;
 }
 
-template <int G, int VPL>
+// Hides a key from the optimiser, so that "c ? a[i] : a[j]" on two entries of
+// a register array stays a two-way select instead of being rewritten as a
+// variable-index extract (a select chain over the whole array).
+__device__ __forceinline__ uint64_t opaque64(uint64_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// Keys a[0..N) into descending order: a bitonic network with compile-time
+// indices, so every key stays in a register.
+template <int N>
+__device__ __forceinline__ void sort_desc(uint64_t (&a)[N]) {
+#pragma unroll
+  for (int size = 2; size <= N; size <<= 1)
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1)
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const uint64_t x = opaque64(a[i]), y = opaque64(a[j]);
+          const bool gt = x > y;
+          const uint64_t hi = gt ? x : y, lo = gt ? y : x;
+          if ((i & size) == 0) {  // descending pair (the final pass, size = N, is descending throughout)
+            a[i] = hi;
+            a[j] = lo;
+          } else {
+            a[i] = lo;
+            a[j] = hi;
+          }
+        }
+      }
+}
+
+// KW: keys a lane keeps after sorting: a lane gives up at most min(k, VPL) keys,
+// so with k <= KW or KW = VPL its head after any round < k is among its KW
+// largest. KMAX: the largest k the instantiation takes (it sizes the result slots).
+template <int G, int VPL, int KW, int KMAX>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits,
                                                          int32_t* __restrict__ idx,
                                                          float* __restrict__ w, int64_t T, int E,
                                                          int k) {
   constexpr int kTokensPerWave = kWave / G;
+  constexpr int NS = (KMAX + G - 1) / G;  // result slots per lane: round r goes to lane r % G, slot r / G
   const int lane = lane_id();
   const int g = lane % G;
   const int64_t wave = static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave;
   const int64_t t = wave * kTokensPerWave + lane / G;
   const bool active = t < T;
 
+  // All VPL loads are issued before any is used: a lane with nothing to load
+  // reads element 0 (T >= 1) and its key is set to zero afterwards, so no load
+  // sits behind a branch that would wait for it.
+  float x[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    const int e = g + v * G;
+    x[v] = logits[active && e < E ? t * E + e : 0];
+  }
   uint64_t key[VPL];
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
     const int e = g + v * G;
-    key[v] = 0;
-    if (active && e < E) {
-      const float x = logits[t * E + e];
-      key[v] = (static_cast<uint64_t>(orderable(x)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(e));
-    }
+    const uint64_t kv = (static_cast<uint64_t>(orderable(x[v])) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(e));
+    key[v] = active && e < E ? kv : 0;
   }
+  sort_desc(key);
 
-  // Round r's result is kept by lane r % G in slot r / G (r < k <= E <= G*VPL).
-  float sel_val[VPL];
-  int sel_id[VPL];
+  float sel_val[NS];
+  int sel_id[NS];
 #pragma unroll
-  for (int s = 0; s < VPL; ++s) {
+  for (int s = 0; s < NS; ++s) {
     sel_val[s] = 0.f;
     sel_id[s] = 0;
   }
   float top = 0.f, sum = 0.f;
   for (int r = 0; r < k; ++r) {
-    uint64_t best = key[0];
+    // the group's largest remaining key is the largest of the lanes' heads; its
+    // owner (keys are unique) drops its head
+    const uint64_t best = group_max<G>(key[0]);
+    const bool own = key[0] == best;
 #pragma unroll
-    for (int v = 1; v < VPL; ++v) best = key[v] > best ? key[v] : best;
-    best = group_max<G>(best);
-#pragma unroll
-    for (int v = 0; v < VPL; ++v)
-      if (key[v] == best) key[v] = 0;  // keys are unique: only the owner matches
+    for (int i = 0; i + 1 < KW; ++i) key[i] = own ? opaque64(key[i + 1]) : opaque64(key[i]);
+    key[KW - 1] = own ? 0 : key[KW - 1];
     const float val = from_orderable(static_cast<uint32_t>(best >> 32));
     const int id = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(best));
     if (r == 0) top = val;
     sum += expf(val - top);
     if (r % G == g) {
 #pragma unroll
-      for (int s = 0; s < VPL; ++s)
+      for (int s = 0; s < NS; ++s)
         if (s == r / G) {
           sel_val[s] = val;
           sel_id[s] = id;
@@ -123,7 +168,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   if (!active) return;
   const float inv = 1.0f / sum;
 #pragma unroll
-  for (int s = 0; s < VPL; ++s) {
+  for (int s = 0; s < NS; ++s) {
     const int r = s * G + g;
     if (r < k) {
       idx[t * k + r] = sel_id[s];
@@ -132,15 +177,22 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   }
 }
 
-template <int G, int VPL>
-hipError_t launch_g(const float* logits, int32_t* idx, float* w, int64_t T, int E, int k,
-                    hipStream_t stream) {
+template <int G, int VPL, int KW, int KMAX>
+hipError_t launch_gk(const float* logits, int32_t* idx, float* w, int64_t T, int E, int k, hipStream_t stream) {
   constexpr int kThreads = 256;
   constexpr int64_t kTokensPerBlock = (kThreads / kWave) * (kWave / G);
   const int64_t blocks = (T + kTokensPerBlock - 1) / kTokensPerBlock;
-  hipLaunchKernelGGL((route_topk_kernel<G, VPL>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
-                     0, stream, logits, idx, w, T, E, k);
+  hipLaunchKernelGGL((route_topk_kernel<G, VPL, KW, KMAX>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                     stream, logits, idx, w, T, E, k);
   return hipGetLastError();
+}
+
+// k <= 8 (every workload) keeps at most 8 keys per lane after the sort
+template <int G, int VPL>
+hipError_t launch_g(const float* logits, int32_t* idx, float* w, int64_t T, int E, int k, hipStream_t stream) {
+  constexpr int KW8 = VPL < 8 ? VPL : 8;
+  if (k <= KW8) return launch_gk<G, VPL, KW8, KW8>(logits, idx, w, T, E, k, stream);
+  return launch_gk<G, VPL, VPL, G * VPL>(logits, idx, w, T, E, k, stream);
 }
 
 }  // namespace
