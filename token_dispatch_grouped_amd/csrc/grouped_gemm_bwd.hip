@@ -363,12 +363,88 @@ __device__ __forceinline__ void bwd_tile(uint16_t* smem, const Operand& opa, con
       }
     }
   };
+  if constexpr (EPI == kSwigluBwd && MODE == kNT) {
+    // dH goes through LDS (the stage buffers are free after the K loop), 128 rows
+    // at a time, so that G, U, dG and dU move as 16-byte vectors of 8 columns and
+    // every thread has all its loads in flight before it waits.
+    constexpr int kPitch = 256 + 4;  // floats per staged row (16 bytes of padding against bank conflicts)
+    float* stg = reinterpret_cast<float*>(smem);
+    const int tid = static_cast<int>(threadIdx.x);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(gu, static_cast<uint32_t>(c_rows) * static_cast<uint32_t>(ldc) * 2u);
+    // one staged block: rows row_base.. of the staging area, lane column col
+    auto stage_block = [&](const f32x16_t& a, int row_base, int col) {
 #pragma unroll
-  for (int ni = 0; ni < NI; ++ni)
+      for (int r = 0; r < 16; ++r)
+        stg[(row_base + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * kPitch + col] = a[r];
+    };
+    // rows [row0, row0 + NR) of the tile, staged from row 0 of the area
+    auto finish_rows = [&](int row0, auto nr_c) {
+      constexpr int NR = decltype(nr_c)::value;
+      constexpr int kChunks = NR * 256 / 8 / kThreads;  // 8-column chunks per thread
+      __syncthreads();                                   // the staged rows are in LDS
+      uint4 gv[kChunks], uv[kChunks];
+      uint32_t go[kChunks], uo[kChunks];
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) store_block(acc[mi][ni], wm * 128 + mi * 32, wn * 128 + blk(ni) * 32 + l31);
+      for (int i = 0; i < kChunks; ++i) {
+        const int c = tid + i * kThreads, rl = c >> 5, col = (c & 31) * 8;
+        const uint32_t ro = static_cast<uint32_t>(row0 + rl) * static_cast<uint32_t>(ldc) * 2u;
+        go[i] = col < c_cols ? ro + static_cast<uint32_t>(col) * 2u : 0x80000000u;
+        uo[i] = col < c_cols ? ro + static_cast<uint32_t>(up_off + col) * 2u : 0x80000000u;
+        gv[i] = buffer_load16(rg, go[i]);
+        uv[i] = buffer_load16(rg, uo[i]);
+      }
 #pragma unroll
-  for (int x = 0; x < MX; ++x) store_block(acc_x[x], 256, wn * 128 + blk(x) * 32 + l31);
+      for (int i = 0; i < kChunks; ++i) {
+        const int c = tid + i * kThreads, rl = c >> 5, col = (c & 31) * 8;
+        const float4 h0 = *reinterpret_cast<const float4*>(stg + rl * kPitch + col);
+        const float4 h1 = *reinterpret_cast<const float4*>(stg + rl * kPitch + col + 4);
+        const float dh[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+        const uint32_t gw[4] = {gv[i].x, gv[i].y, gv[i].z, gv[i].w}, uw[4] = {uv[i].x, uv[i].y, uv[i].z, uv[i].w};
+        uint32_t dgw[4], duw[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t dgp = 0, dup = 0;
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const float g = bf16_to_f32(static_cast<uint16_t>(gw[q] >> (16 * hh)));
+            const float u = bf16_to_f32(static_cast<uint16_t>(uw[q] >> (16 * hh)));
+            const float s = sigmoid_fast(g);
+            const float d = dh[2 * q + hh];
+            dgp |= static_cast<uint32_t>(f32_to_bf16_rne(d * u * (s * (1.0f + g * (1.0f - s))))) << (16 * hh);
+            dup |= static_cast<uint32_t>(f32_to_bf16_rne(d * g * s)) << (16 * hh);
+          }
+          dgw[q] = dgp;
+          duw[q] = dup;
+        }
+        buffer_store16(make_uint4(dgw[0], dgw[1], dgw[2], dgw[3]), rc, go[i]);
+        buffer_store16(make_uint4(duw[0], duw[1], duw[2], duw[3]), rc, uo[i]);
+      }
+      __syncthreads();  // everyone has read the staged rows before the next rows are staged
+    };
+    __syncthreads();  // every wave is done with the K loop's LDS stages
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (wm == h) {
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi) stage_block(acc[mi][ni], mi * 32, wn * 128 + blk(ni) * 32 + l31);
+      }
+      finish_rows(h * 128, std::integral_constant<int, 128>{});
+    }
+    if constexpr (MX > 0) {
+#pragma unroll
+      for (int x = 0; x < MX; ++x) stage_block(acc_x[x], 0, wn * 128 + blk(x) * 32 + l31);
+      finish_rows(256, std::integral_constant<int, 32>{});
+    }
+  } else {
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) store_block(acc[mi][ni], wm * 128 + mi * 32, wn * 128 + blk(ni) * 32 + l31);
+#pragma unroll
+    for (int x = 0; x < MX; ++x) store_block(acc_x[x], 256, wn * 128 + blk(x) * 32 + l31);
+  }
 }
 
 // NT: C[rows, N] = A[rows, K] @ B_e[N, K]^T over row tiles of each local expert.
