@@ -94,7 +94,9 @@ def test_route_topk_ties_and_signed_zeros(E, k):
                                          (5, 128, 4, 0, 128), (1025, 16, 16, 3, 4),
                                          # either side of the single-workgroup path (at most 2048 pairs)
                                          (2047, 8, 1, 0, 8), (1024, 1024, 2, 512, 1024), (683, 128, 3, 16, 32),
-                                         (1, 1024, 1024, 0, 1024), (256, 256, 8, 0, 32)])
+                                         (1, 1024, 1024, 0, 1024), (256, 256, 8, 0, 32),
+                                         # an ep8_share128-sized table (128 experts x 128 chunks) and one chunk more
+                                         (8192, 128, 4, 0, 16), (8193, 128, 4, 112, 128)])
 def test_dispatch_matches_oracle(T, E, k, lo, hi):
     rng = np.random.default_rng(T + E + k)
     logits = rng.standard_normal((T, E)).astype(np.float32)
