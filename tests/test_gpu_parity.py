@@ -254,6 +254,49 @@ def test_layer_every_tile_height():
     assert [int((top1 == e).sum()) for e in range(E)] == counts
 
 
+def _fused_matches_staged(w, logits, res, ref):
+    x = mi.hidden_states(w)
+    wgu, wdn = mi.expert_weights(w)
+    fused = moe.layer(g.to_dev(x, w.dtype), g.to_dev(logits, "f32"), g.to_dev(wgu, w.dtype),
+                      g.to_dev(wdn, w.dtype), w.k, w.e_begin, w.e_end, fused=True)
+    torch.cuda.synchronize()
+    n_loc = ref["x_perm"].shape[0]
+    assert torch.equal(fused["h"][:n_loc], res["h"][:n_loc])
+    assert torch.equal(fused["y"][:n_loc], res["y"][:n_loc])
+    assert torch.equal(fused["out"], res["out"])
+
+
+@pytest.mark.parametrize("counts", [
+    [129, 255, 256, 257, 288, 289, 300, 350, 400, 513, 544],  # rows > 128: 256/288-row tiles, 64/128/256-row tails
+    [65, 100, 128],  # 128-row tiles
+    [33, 50, 64],  # 64-row tiles
+    [1, 16, 31, 32],  # 32-row tiles
+], ids=["over128", "to128", "to64", "to32"])
+def test_layer_split_last_round_every_tile_height(counts):
+    """Experts of one height class among 64 local experts, the rest empty: the
+    grid (sized for the worst case) is more than twice the tile count, so both
+    GEMMs run their only round as half-width tiles, and the second half of each
+    last column block (d_ff = 160 and d = 320 leave it at most half full) has
+    no columns."""
+    counts = counts + [0] * (64 - len(counts))
+    E = len(counts)
+    w = mi.Workload("split_tile_heights", int(sum(counts)), 320, 160, E, 1, 0, E, "bf16", 31)
+    logits = _one_hot_logits(counts, E, 31)
+    res, ref = _layer_case(w, logits)
+    top1 = ref["idx"][:, 0]
+    assert [int((top1 == e).sum()) for e in range(E)] == counts
+    _fused_matches_staged(w, logits, res, ref)
+
+
+def test_layer_split_after_full_rounds():
+    """64 experts of 77 to 121 rows (one height class) and nine gate/up column
+    blocks: 576 tiles, two full rounds on 256 workgroups and a third of 64 tiles
+    run as 128 half tiles."""
+    w = mi.Workload("split_after_rounds", 3072, 256, 1152, 64, 2, 0, 64, "bf16", 32)
+    res, ref = _layer_case(w)
+    _fused_matches_staged(w, mi.router_logits(w), res, ref)
+
+
 @pytest.mark.parametrize("w", [SMALL[3], SMALL[4], mi.Workload("regs_heights", 600, 256, 192, 8, 2, 0, 8, "bf16", 24)],
                          ids=["skew_small", "decode_small", "heights"])
 def test_layer_register_staged_kernel(w, monkeypatch):

@@ -104,6 +104,7 @@ struct SortedTileMap {
   int mstart[kMaxExperts + 1];  // row-tile prefix over positions
   int eid[kMaxExperts];         // local expert at each position
   int rstart[kMaxExperts + 1];  // first row of each expert (by expert id), relative to the local segment
+  int classes;                  // height classes that hold at least one expert with rows
 };
 
 __device__ __forceinline__ int height_class(int rows) {
@@ -129,7 +130,10 @@ __device__ void build_sorted_tile_map(SortedTileMap& tm, const int32_t* __restri
 #pragma unroll
       for (int q = 0; q < 5; ++q) cnt[q] += __popcll(__ballot(c == q));
     }
-    if (lane == 0) tm.rstart[e_loc] = min(offsets[e_begin + e_loc] - base, n_max);
+    if (lane == 0) {
+      tm.rstart[e_loc] = min(offsets[e_begin + e_loc] - base, n_max);
+      tm.classes = (cnt[0] > 0) + (cnt[1] > 0) + (cnt[2] > 0) + (cnt[3] > 0);
+    }
     int cbase[5];
     cbase[0] = 0;
 #pragma unroll

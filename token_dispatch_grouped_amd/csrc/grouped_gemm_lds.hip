@@ -60,21 +60,27 @@ struct Frags {
 
 // H = rows of the tile: 32, 64, 128, 256 or 288. A 288-row tile is a 256-row
 // tile plus one 32-row block (rows 256..287) that every wave shares: each wave
-// computes it against half of its own weight blocks.
-template <int H>
+// computes it against half of its own weight blocks. BN = weight columns of the
+// tile: 256, or 128 for a half-width tile (the two halves of a tile split for
+// balance, or a last column block that is at most half full).
+template <int H, int BN>
 struct Layout {
   static constexpr int WM = H >= 64 ? 2 : 1;       // waves along M
   static constexpr int WN = 4 / WM;                // waves along N
   static constexpr int MI = H / WM / 32;           // 32-row MFMA blocks per wave (regular part)
-  static constexpr int NI = 256 / WN / 32;         // 32-column MFMA blocks per wave
+  static constexpr int NI = BN / WN / 32;          // 32-column MFMA blocks per wave
   static constexpr int XR = (H - WM * MI * 32) / 32;  // shared extra row blocks (0 or 1)
-  static constexpr int MX = XR ? NI / 2 : 0;       // extra MFMA blocks per wave
+  // extra MFMA blocks per wave: half of four blocks, or one of two (with SwiGLU the
+  // two wave rows then hold the gate and the up half of one pair between them)
+  static constexpr int MX = XR ? (NI == 4 ? 2 : 1) : 0;
   static constexpr int A_INSTR = H / 16;           // 1 KB DMA instructions per activation stage
   static constexpr int A_PER_WAVE = (A_INSTR + 3) / 4;
-  static constexpr int PER = 4 + A_PER_WAVE;       // DMA instructions per stage per wave
+  static constexpr int B_PER_WAVE = BN / 64;       // 1 KB DMA instructions per weight stage, per wave
+  static constexpr int PER = B_PER_WAVE + A_PER_WAVE;  // DMA instructions per stage per wave
   static constexpr int LDS_READS = MI + XR + 2 * NI;
   static constexpr int NMFMA = MI * NI + MX;       // MFMAs per 16-wide K slice
   static_assert(XR == 0 || (XR == 1 && WM == 2), "one shared extra row block, two waves along M");
+  static_assert(BN == 256 || BN == 128, "full or half-width tiles");
 };
 
 // Where activation rows come from: rows of A in order (x_perm, H), or, with
@@ -86,13 +92,19 @@ struct ARows {
   uint32_t a_bytes;         // bytes of A (T * K * 2)
 };
 
-template <bool SWIGLU, bool GATHER, int H>
+template <bool SWIGLU, bool GATHER, int H, int BN>
 __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __restrict__ A,
                                           const uint16_t* __restrict__ Bexp, uint16_t* __restrict__ C,
                                           int row0, int rows_valid, int n0, int K, int N, int ldb,
                                           const ARows& ar) {
-  using L = Layout<H>;
+  using L = Layout<H, BN>;
   constexpr int MI = L::MI, NI = L::NI, WM = L::WM, WN = L::WN, PER = L::PER;
+  // A half-width tile does half the MFMA work per stage, so the same lookahead
+  // in stages covers half the time: it runs five stages (four ahead) in the
+  // room of the full-width tile's four.
+  constexpr int NS = BN == 256 ? kStages : 5;
+  constexpr uint32_t kBBytes = BN * kBK * 2;  // weight stage
+  static_assert(NS * (kAStageBytes + kBBytes) <= kStages * (kAStageBytes + kBStageBytes), "stages fit");
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = uniform(tid / kWave);
@@ -100,7 +112,7 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
   const int ksteps = K / kBK;
 
   const uint32_t sA_base = uniform(static_cast<int>(lds_addr(smem)));
-  const uint32_t sB_base = sA_base + kStages * kAStageBytes;
+  const uint32_t sB_base = sA_base + NS * kAStageBytes;
 
   // ---- DMA: per-lane byte offsets, constant over the tile ---------------------------
   // Activation instruction j covers rows 16j..16j+15: lane L brings row 16j + L/4,
@@ -128,21 +140,22 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
       a_voff[jj] = static_cast<uint32_t>(r) * static_cast<uint32_t>(K) * 2u + static_cast<uint32_t>(c) * 16u;
     }
   }
-  // Weight instruction j covers k-rows 2j, 2j+1 of the stage: lane L brings k-row
-  // 2j + L/32, logical chunk (L & 31) ^ (4 * (k & 3)) (8 columns) into LDS slot L.
-  uint32_t b_voff[4];
+  // Weight instruction j covers RPI k-rows of the stage (2 at BN = 256, 4 at 128):
+  // lane L brings k-row RPI j + L / CPR, logical chunk (L % CPR) ^ (4 * (k & 3))
+  // (8 columns) into LDS slot L. With SwiGLU the first half of a row's chunks are
+  // gate columns and the second half the matching up columns.
+  constexpr int CPR = BN / 8, RPI = 64 / CPR;
+  uint32_t b_voff[L::B_PER_WAVE];
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    const int j = wave * 4 + jj;
-    const int kl = 2 * j + (lane >> 5);
-    const int c = (lane & 31) ^ (4 * (kl & 3));
+  for (int jj = 0; jj < L::B_PER_WAVE; ++jj) {
+    const int j = wave * L::B_PER_WAVE + jj;
+    const int kl = RPI * j + lane / CPR;
+    const int c = (lane % CPR) ^ (4 * (kl & 3));
     int col;
-    if (SWIGLU) col = c < 16 ? n0 + 8 * c : N + n0 + 8 * (c - 16);
+    if (SWIGLU) col = c < CPR / 2 ? n0 + 8 * c : N + n0 + 8 * (c - CPR / 2);
     else col = n0 + 8 * c;
     b_voff[jj] = (static_cast<uint32_t>(kl) * static_cast<uint32_t>(ldb) + static_cast<uint32_t>(col)) * 2u;
   }
-
-
 
   // ---- fragment reads ----------------------------------------------------------------
   const int l31 = lane & 31;
@@ -155,16 +168,20 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
     a_rd_x[kk] = static_cast<uint32_t>((WM * MI * 32 + l31) * kBK + c * 8) * 2u;  // extra row block
   }
   // B-tile column of register slot ni (SwiGLU: slots [0, NI/2) gate, the rest
-  // the matching up columns). In a 288-row tile the second wave row holds its
-  // blocks in swapped slots, so that every wave's share of the extra row block
-  // uses slots 0 and X1 = (SwiGLU ? NI/2 : 1): the gate/up pair, or two plain
-  // blocks, that the other wave row does not take.
+  // the matching up columns; with one block per wave, waves 0 and 1 take gate
+  // blocks and waves 2 and 3 the matching up blocks). In a 288-row tile the
+  // second wave row holds its blocks in swapped slots, so that every wave's
+  // share of the extra row block uses slot 0 (and X1 = (SwiGLU ? NI/2 : 1) when
+  // it takes two): the gate/up pair or plain blocks that the other wave row does
+  // not take. With two blocks per wave that share is one block, and under
+  // SwiGLU the first wave row holds the gate half and the second the up half.
   constexpr int X1 = SWIGLU ? NI / 2 : 1;
   auto bcol = [&](int ni) {
     constexpr int half = NI / 2;
-    if (L::XR) ni = wm ? (SWIGLU ? ni ^ 1 : ni ^ 2) : ni;
-    if (SWIGLU) return ni < half ? wn * (128 / WN) + ni * 32 : 128 + wn * (128 / WN) + (ni - half) * 32;
-    return wn * (256 / WN) + ni * 32;
+    if constexpr (SWIGLU && NI == 1) return wn < 2 ? wn * 32 : BN / 2 + (wn - 2) * 32;
+    if (L::XR) ni = wm ? (SWIGLU || NI == 2 ? ni ^ 1 : ni ^ 2) : ni;
+    if (SWIGLU) return ni < half ? wn * (BN / 2 / WN) + ni * 32 : BN / 2 + wn * (BN / 2 / WN) + (ni - half) * 32;
+    return wn * (BN / WN) + ni * 32;
   };
   uint32_t b_rd[NI];
   {
@@ -173,7 +190,7 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
       const int n = bcol(ni) + (g & 1) * 16 + 4 * (i & 3);
-      b_rd[ni] = static_cast<uint32_t>(kl * 256 + (((n >> 3) ^ (4 * (kl & 3))) * 8) + (n & 4)) * 2u;
+      b_rd[ni] = static_cast<uint32_t>(kl * BN + (((n >> 3) ^ (4 * (kl & 3))) * 8) + (n & 4)) * 2u;
     }
   }
   const uint32_t sA_addr = sA_base, sB_addr = sB_base;
@@ -189,7 +206,7 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
       f.a[MI] = ds_read16<0>(sA_addr + buf * kAStageBytes + a_rd_x[kk]);
     } else {
       constexpr int ni = (r - MI - L::XR) / 2, h = (r - MI - L::XR) % 2;
-      f.b[ni][h] = ds_read_tr<kk * 8192 + h * 2048>(sB_addr + buf * kBStageBytes + b_rd[ni]);
+      f.b[ni][h] = ds_read_tr<kk * 32 * BN + h * 8 * BN>(sB_addr + buf * kBBytes + b_rd[ni]);
     }
   };
   auto tie_frags = [&](Frags& f) {
@@ -238,25 +255,31 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
     uint32_t la, lb;  // LDS byte addresses of the stage's buffers
   };
   auto stage_loads = [&](int s) {
-    const int buf = s % kStages;
+    const int buf = s % NS;
     return StageLoads{make_rsrc(a_tile + s * kBK, a_bytes - static_cast<uint32_t>(s) * kBK * 2u),
                       make_rsrc(Bexp + static_cast<int64_t>(s) * kBK * ldb,
                                 b_bytes - static_cast<uint32_t>(s) * kBK * ldb * 2u),
-                      sA_base + buf * kAStageBytes, sB_base + buf * kBStageBytes};
+                      sA_base + buf * kAStageBytes, sB_base + buf * kBBytes};
   };
-  // load j of a stage: j < A_PER_WAVE activations, then this wave's 4 weight loads
+  // load j of a stage: j < A_PER_WAVE activations, then this wave's B_PER_WAVE weight loads
   auto dma_one = [&](const StageLoads& st, auto j_c) {
     constexpr int j = decltype(j_c)::value;
     if constexpr (j < L::A_PER_WAVE) dma16(st.ra, a_voff[j], st.la + a_slot[j] * 1024);
-    else dma16(st.rb, b_voff[j - L::A_PER_WAVE], st.lb + (wave * 4 + (j - L::A_PER_WAVE)) * 1024);
+    else dma16(st.rb, b_voff[j - L::A_PER_WAVE], st.lb + (wave * L::B_PER_WAVE + (j - L::A_PER_WAVE)) * 1024);
   };
 
   // ---- pipeline -------------------------------------------------------------------------
-  // Stage s lands in buffer s % kStages; it is issued three stages ahead. When a
-  // wave waits for stage s, min(kStages - 2, ksteps - 1 - s) later stages of its
-  // own loads may still be in flight.
+  // Stage s lands in buffer s % NS; it is issued NS - 1 stages ahead. When a
+  // wave waits for stage s, min(NS - 2, ksteps - 1 - s) later stages of its own
+  // loads may still be in flight.
   auto wait_stage = [&](int s) {
-    const int after = min(kStages - 2, ksteps - 1 - s);
+    const int after = min(NS - 2, ksteps - 1 - s);
+    if constexpr (NS > 4) {
+      if (after >= 3) {
+        wait_vmcnt<3 * PER>();
+        return;
+      }
+    }
     if (after >= 2) wait_vmcnt<2 * PER>();
     else if (after == 1) wait_vmcnt<PER>();
     else wait_vmcnt<0>();
@@ -269,11 +292,11 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
   // every DMA load is issued in the shadow of an MFMA: slice 0 (fragments f0)
   // carries slice 1's reads, one per MFMA; then the stage barrier; slice 1
   // carries the next stage's slice-0 reads, one per MFMA, and the DMA of stage
-  // ks + kStages, one per two MFMAs.
+  // ks + NS, one per two MFMAs.
   Frags f0, f1;
   auto stage = [&](int ks, auto dma_c, auto more_c) {
     constexpr bool DMA = decltype(dma_c)::value, MORE = decltype(more_c)::value;
-    const int buf = ks % kStages;
+    const int buf = ks % NS;
     wait_lgkmcnt<0>();  // f0 (read during the previous stage) has landed
     tie_frags(f0);
     __builtin_amdgcn_sched_barrier(0);
@@ -292,8 +315,8 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
     }
     __builtin_amdgcn_sched_barrier(0);
     StageLoads st;
-    if constexpr (DMA) st = stage_loads(ks + kStages);
-    const int nbuf = (ks + 1) % kStages;
+    if constexpr (DMA) st = stage_loads(ks + NS);
+    const int nbuf = (ks + 1) % NS;
     static_for<0, NM>([&](auto q_c) {
       constexpr int q = decltype(q_c)::value;
       mfma_one(f1, q_c);
@@ -307,22 +330,22 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // prologue: stages 0..kStages-2 in flight, stage 0 landed, stage kStages-1
+  // prologue: stages 0..NS-2 in flight, stage 0 landed, stage NS-1
   // issued, slice 0 of stage 0 requested
-  for (int s = 0; s < kStages - 1 && s < ksteps; ++s) {
+  for (int s = 0; s < NS - 1 && s < ksteps; ++s) {
     const StageLoads st = stage_loads(s);
     static_for<0, PER>([&](auto j) { dma_one(st, j); });
   }
   wait_stage(0);
   __builtin_amdgcn_s_barrier();
-  if (kStages - 1 < ksteps) {
-    const StageLoads st = stage_loads(kStages - 1);
+  if (NS - 1 < ksteps) {
+    const StageLoads st = stage_loads(NS - 1);
     static_for<0, PER>([&](auto j) { dma_one(st, j); });
   }
   static_for<0, R>([&](auto r) { read_one(f0, 0, K0{}, r); });
 
   int ks = 0;
-  for (; ks + kStages < ksteps; ++ks) stage(ks, std::true_type{}, std::true_type{});
+  for (; ks + NS < ksteps; ++ks) stage(ks, std::true_type{}, std::true_type{});
   for (; ks + 1 < ksteps; ++ks) stage(ks, std::false_type{}, std::true_type{});
   stage(ks, std::false_type{}, std::false_type{});
 
@@ -334,40 +357,114 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
     const int col = n0 + bcol(ni) + l31;
     return col < N ? static_cast<uint32_t>(col) * 2u : 0x80000000u;
   };
-  constexpr int kStoreBlocks = SWIGLU ? NI / 2 : NI;
-  uint32_t coff[kStoreBlocks];
+  auto store = [&](float v, int row, uint32_t coff) {
+    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(v), rc_src,
+                                          static_cast<int>(static_cast<uint32_t>(row) * c_row_bytes + coff), 0, 0);
+  };
+  auto acc_row = [&](int r) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); };  // row of element r in a block
+
+  // Where a gate block and its up block sit in different waves (one block per
+  // wave; or the shared extra row block of a half-width 288-row tile), the up
+  // wave hands its 16 accumulators per lane over through LDS, in the activation
+  // buffer the last stages left untouched (stage ksteps - NS's, free since its barrier).
+  constexpr bool XCH_MAIN = SWIGLU && NI == 1;
+  constexpr bool XCH_X = SWIGLU && L::MX == 1;
+  float up_in[16];
+  if constexpr (XCH_MAIN || XCH_X) {
+    const uint32_t xbyte = (ksteps % NS) * kAStageBytes;
+    float* xch = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) + xbyte);
+    const bool giver = XCH_MAIN ? wn >= 2 : wm == 1;
+    const int slot = XCH_MAIN ? (wn & 1) : wn;
+    float4* mine = reinterpret_cast<float4*>(xch) + slot * 256 + lane;
+    if (giver) {
+      const f32x16_t& v = XCH_MAIN ? acc[0][0] : acc_x[0];
 #pragma unroll
-  for (int ni = 0; ni < kStoreBlocks; ++ni) coff[ni] = col_off(ni);
+      for (int j = 0; j < 4; ++j) mine[64 * j] = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
+    }
+    __syncthreads();
+    if (!giver) {
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = wm * (MI * 32) + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-      const uint32_t row_off = static_cast<uint32_t>(row) * c_row_bytes;
-#pragma unroll
-      for (int ni = 0; ni < kStoreBlocks; ++ni) {
-        const float v = SWIGLU ? silu_fast(acc[mi][ni][r]) * acc[mi][ni + NI / 2][r] : acc[mi][ni][r];
-        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(v), rc_src, static_cast<int>(row_off + coff[ni]), 0,
-                                              0);
+      for (int j = 0; j < 4; ++j) {
+        const float4 u = mine[64 * j];
+        up_in[4 * j] = u.x;
+        up_in[4 * j + 1] = u.y;
+        up_in[4 * j + 2] = u.z;
+        up_in[4 * j + 3] = u.w;
       }
     }
   }
-  if constexpr (L::MX > 0) {  // the extra row block: slot 0 (with its up pair X1 for SwiGLU), or slots 0 and 1
+
+  if constexpr (XCH_MAIN) {  // 32 rows: waves 0 and 1 write silu(gate) * up
+    if (wn < 2) {
+      const uint32_t coff = col_off(0);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = WM * MI * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-      const uint32_t row_off = static_cast<uint32_t>(row) * c_row_bytes;
-      if constexpr (SWIGLU) {
-        const float v = silu_fast(acc_x[0][r]) * acc_x[1][r];
-        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(v), rc_src, static_cast<int>(row_off + coff[0]), 0, 0);
-      } else {
+      for (int r = 0; r < 16; ++r) store(silu_fast(acc[0][0][r]) * up_in[r], acc_row(r), coff);
+    }
+  } else if constexpr (SWIGLU && NI == 2 && L::XR) {
+    // half-width 288-row tile: the second wave row holds its up block in slot 0
+    const int gs = wm;  // gate slot
+    const uint32_t coff = col_off(gs);
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
-          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(acc_x[x][r]), rc_src,
-                                                static_cast<int>(row_off + coff[x]), 0, 0);
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float a0 = acc[mi][0][r], a1 = acc[mi][1][r];
+        store(gs ? silu_fast(a1) * a0 : silu_fast(a0) * a1, wm * (MI * 32) + mi * 32 + acc_row(r), coff);
+      }
+  } else {
+    constexpr int kStoreBlocks = SWIGLU ? NI / 2 : NI;
+    uint32_t coff[kStoreBlocks];
+#pragma unroll
+    for (int ni = 0; ni < kStoreBlocks; ++ni) coff[ni] = col_off(ni);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * (MI * 32) + mi * 32 + acc_row(r);
+#pragma unroll
+        for (int ni = 0; ni < kStoreBlocks; ++ni)
+          store(SWIGLU ? silu_fast(acc[mi][ni][r]) * acc[mi][ni + NI / 2][r] : acc[mi][ni][r], row, coff[ni]);
       }
     }
   }
+  if constexpr (L::MX > 0) {  // the extra row block (rows WM * MI * 32 ...)
+    const int row0x = WM * MI * 32;
+    if constexpr (XCH_X) {  // gate half here in the first wave row, up half handed over by the second
+      if (wm == 0) {
+        const uint32_t coff = col_off(0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) store(silu_fast(acc_x[0][r]) * up_in[r], row0x + acc_row(r), coff);
+      }
+    } else if constexpr (SWIGLU) {  // slot 0 with its up pair X1
+      const uint32_t coff = col_off(0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) store(silu_fast(acc_x[0][r]) * acc_x[1][r], row0x + acc_row(r), coff);
+    } else {  // slots 0 .. MX-1
+#pragma unroll
+      for (int x = 0; x < L::MX; ++x) {
+        const uint32_t coff = col_off(x);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) store(acc_x[x][r], row0x + acc_row(r), coff);
+      }
+    }
+  }
+}
+
+// The tile height for rows_valid rows (a last row tile is the smallest that covers them).
+template <bool SWIGLU, bool GATHER, int BN>
+__device__ __forceinline__ void run_tile(uint16_t* smem, const uint16_t* __restrict__ A,
+                                         const uint16_t* __restrict__ Bexp, uint16_t* __restrict__ C, int row0,
+                                         int rows_valid, int n0, int K, int N, int ldb, const ARows& ar) {
+  if (rows_valid > 256)
+    gemm_tile<SWIGLU, GATHER, 288, BN>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb, ar);
+  else if (rows_valid > 128)
+    gemm_tile<SWIGLU, GATHER, 256, BN>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb, ar);
+  else if (rows_valid > 64)
+    gemm_tile<SWIGLU, GATHER, 128, BN>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb, ar);
+  else if (rows_valid > 32)
+    gemm_tile<SWIGLU, GATHER, 64, BN>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb, ar);
+  else
+    gemm_tile<SWIGLU, GATHER, 32, BN>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb, ar);
 }
 
 template <bool SWIGLU, bool GATHER>
@@ -387,26 +484,42 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_lds_kernel(
   ARows ar{nullptr, k, a_bytes};
   if (GATHER) ar.perm_seg = perm + offsets[e_begin];
 
+  // Balance: when the last round would keep at most half of the workgroups busy
+  // and every expert's tiles have the same height class (so that the rounds
+  // before it end together), its tiles are split into half-width tiles, two per
+  // tile, and that round takes a little over half as long. (With mixed classes
+  // the workgroups that would take the halves include ones whose earlier tiles
+  // were the costly ones.) A last column block with at most half of its columns
+  // in range is computed as a half-width tile when it has more than 32 rows (a
+  // 32-row tile streams weights, and measured no faster at half width).
   const int G = gridDim.x, r = xcd_remap(blockIdx.x, G);
+  const int rounds = (total + G - 1) / G;
+  const int last = total - (rounds - 1) * G;
+  const bool split = total > 0 && 2 * last <= G && uniform(tm.classes) == 1;
+  const bool narrow_last = N - (n_tiles - 1) * kOutCols <= kOutCols / 2;
   for (int i = 0;; ++i) {
-    const int tile = snake_tile(i, r, G);
-    if (tile >= total) break;  // later rounds hold only larger ids
+    int tile, part = 0;  // part: 0 the whole tile, 1 or 2 its first or second half
+    if (split && i == rounds - 1) {
+      const int h = (i & 1) ? G - 1 - r : r;  // half tiles in the snake's direction
+      if (h >= 2 * last) break;
+      tile = (rounds - 1) * G + (h >> 1);
+      part = 1 + (h & 1);
+    } else {
+      tile = snake_tile(i, r, G);
+      if (tile >= total) break;  // later rounds hold only larger ids
+    }
     const SortedTile tc = find_sorted_tile(tm, tile, n_tiles, e_loc);
     const int row0 = uniform(tm.rstart[tc.e]) + tc.mt * 256;
     const int row_end = uniform(tm.rstart[tc.e + 1]);
     const int rows_valid = tc.mt == tc.mt_e - 1 ? row_end - row0 : 256;
-    const int n0 = tc.nt * kOutCols;
+    const int n0 = tc.nt * kOutCols + (part == 2 ? kOutCols / 2 : 0);
+    if (n0 >= N) break;  // second half of a last column block that is at most half full
+    const bool half = part != 0 || (narrow_last && tc.nt == n_tiles - 1 && rows_valid > 32);
     const uint16_t* Bexp = B + static_cast<int64_t>(tc.e) * b_expert;
-    if (rows_valid > 256)
-      gemm_tile<SWIGLU, GATHER, 288>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb, ar);
-    else if (rows_valid > 128)
-      gemm_tile<SWIGLU, GATHER, 256>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb, ar);
-    else if (rows_valid > 64)
-      gemm_tile<SWIGLU, GATHER, 128>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb, ar);
-    else if (rows_valid > 32)
-      gemm_tile<SWIGLU, GATHER, 64>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb, ar);
+    if (half)
+      run_tile<SWIGLU, GATHER, 128>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb, ar);
     else
-      gemm_tile<SWIGLU, GATHER, 32>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb, ar);
+      run_tile<SWIGLU, GATHER, 256>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb, ar);
     // every wave has waited for its last LDS reads; the next tile's loads may land
     __builtin_amdgcn_s_barrier();
   }
