@@ -199,10 +199,12 @@ def main() -> int:
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
 
+    gu = None  # training: the gate/up pre-activations the forward keeps for the backward
+
     def gemm():
         if fused:
             moe.grouped_gemm_gather(dx, disp.perm, disp.offsets, dgu, ddn, w.k, w.E, w.e_begin, w.e_end,
-                                    h=h, y=y, stream=cur())
+                                    h=h, y=y, stream=cur(), gu=gu)
         else:
             moe.grouped_gemm(disp.x_perm, disp.offsets, dgu, ddn, w.T, w.k, w.E, w.e_begin, w.e_end,
                              h=h, y=y, stream=cur())
@@ -222,10 +224,12 @@ def main() -> int:
         d_logits = torch.empty((w.T, w.E), dtype=torch.float32, device=dev)
         ws_bytes = moe.grouped_gemm_backward_workspace_bytes(w.T, w.d, w.d_ff, w.E, w.k, w.e_begin, w.e_end)
         bws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        gu = torch.empty((w.n_max, 2 * w.d_ff), dtype=dx.dtype, device=dev)
 
     def bwd_gemm():
         moe.grouped_gemm_backward(dx, disp.perm, disp.offsets, dgu, ddn, h, d_y, w.k, w.E, w.e_begin, w.e_end,
-                                  d_x_perm=d_xp, d_w_gate_up=d_wgu, d_w_down=d_wdn, workspace=bws, stream=cur())
+                                  d_x_perm=d_xp, d_w_gate_up=d_wgu, d_w_down=d_wdn, workspace=bws, stream=cur(),
+                                  gu=gu)
 
     # the calls of one step, in order: (name, call)
     calls = [
@@ -294,17 +298,17 @@ def main() -> int:
         torch.cuda.synchronize()
     gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
-    # forward: gate/up (4 N d d_ff) + down (2 N d d_ff); backward: recomputed gate/up (4), dH (2),
-    # dX (4), dW_dn (2), dW_gu (4)
-    flops = (16.0 if train else 6.0) * n_loc * w.d * w.d_ff
+    # forward: gate/up (4 N d d_ff) + down (2 N d d_ff); backward (the forward kept the gate/up
+    # pre-activations): dH (2), dX (4), dW_dn (2), dW_gu (4)
+    flops = (12.0 if train else 6.0) * n_loc * w.d * w.d_ff
     b = 2 if w.dtype == "bf16" else 4
     # forward: weights of every active local expert once, one activation row per local pair and
-    # H read once, H and Y written once. backward: W_gu read twice and W_dn once, both weight
-    # gradients written once (8 d d_ff per active expert); per local row, the d-wide blocks
-    # moved 7 times (x, x_perm, dY twice, dX) and the d_ff-wide ones 11 times (gate/up written
-    # and read, their gradient written and read twice, H read)
+    # H read once, H and Y written once. backward: W_gu and W_dn read once, both weight gradients
+    # written once (6 d d_ff per active expert); per local row, the d-wide blocks moved 6 times
+    # (x read, x_perm written and read, dY read twice, dX written) and the d_ff-wide ones 9 times
+    # (the kept gate/up read, their gradient written and read twice, H read)
     if train:
-        gemm_bytes = 8.0 * active * w.d * w.d_ff * b + n_loc * (7.0 * w.d + 11.0 * w.d_ff) * b
+        gemm_bytes = 6.0 * active * w.d * w.d_ff * b + n_loc * (6.0 * w.d + 9.0 * w.d_ff) * b
     else:
         gemm_bytes = 3.0 * active * w.d * w.d_ff * b + 2.0 * n_loc * (w.d + w.d_ff) * b
     peak_flops = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
@@ -316,8 +320,8 @@ def main() -> int:
         bound = "mfma" if w.dtype == "bf16" else "alu"
         achieved, peak, unit = flops / t_gemm / 1e12, peak_flops, "TFLOP/s"
     roofline = {
-        "kernel": ("moe_grouped_gemm_backward (row gather, gate/up recompute, dH+SwiGLU backward, dX, "
-                   "dW_down, dW_gate_up launches)" if train else
+        "kernel": ("moe_grouped_gemm_backward_saved (row gather, dH+SwiGLU backward, dX, dW_down, "
+                   "dW_gate_up launches; gate/up pre-activations kept by the forward)" if train else
                    ("moe_grouped_gemm_gather" if fused else "moe_grouped_gemm")
                    + " (gate/up+SwiGLU launch, then down launch)"),
         "bound": bound,

@@ -238,6 +238,37 @@ moe_status moe_grouped_gemm_backward(const moe_shape* s, moe_dtype dt, const voi
 moe_status moe_dispatch_backward(const moe_shape* s, moe_dtype dt, const void* d_x_perm,
                                  const int32_t* pair_pos, void* d_x, hipStream_t stream);
 
+/* Training pair: a forward that keeps the gate/up pre-activations and a
+ * backward that takes them instead of recomputing them (one grouped GEMM of
+ * 4 N_loc d d_ff FLOP fewer, for 2 N_max d_ff elements of device memory).
+ * Same computation and sources as moe_grouped_gemm_gather and
+ * moe_grouped_gemm_backward above.
+ *
+ * moe_grouped_gemm_gather_save: moe_grouped_gemm_gather (same h and y, bit for
+ * bit), and also
+ *   gu        [N_max, 2*d_ff] dt, written: rows [0, N_loc) hold [G | U] = X_R @
+ *             W_gu[e] for each local row (G in columns [0, d_ff), U after it),
+ *             rounded to dt from the fp32 accumulators that h is formed from.
+ * MOE_EINVAL if gu is NULL with T > 0; otherwise as moe_grouped_gemm_gather. */
+moe_status moe_grouped_gemm_gather_save(const moe_shape* s, moe_dtype dt, const void* x,
+                                        const int32_t* perm, const int32_t* offsets,
+                                        const void* w_gate_up, const void* w_down, void* h, void* y,
+                                        void* gu, void* workspace, hipStream_t stream);
+
+/* moe_grouped_gemm_backward with [G | U] read from gu (as written by
+ * moe_grouped_gemm_gather_save for the same x, perm, offsets and w_gate_up)
+ * rather than recomputed: the same gradients, bit for bit. Arguments as for
+ * moe_grouped_gemm_backward, plus
+ *   gu        [N_max, 2*d_ff] dt, read only.
+ * The workspace is the same size (its [G | U] part goes unused).
+ * MOE_EINVAL if gu is NULL with T > 0; otherwise as moe_grouped_gemm_backward. */
+moe_status moe_grouped_gemm_backward_saved(const moe_shape* s, moe_dtype dt, const void* x,
+                                           const int32_t* perm, const int32_t* offsets,
+                                           const void* w_gate_up, const void* w_down,
+                                           const void* h, const void* gu, const void* d_y,
+                                           void* d_x_perm, void* d_w_gate_up, void* d_w_down,
+                                           void* workspace, hipStream_t stream);
+
 /* Gradient of the combine weights of moe_route_topk w.r.t. the logits (softmax
  * over the selected logits; the selection passes no gradient):
  *     d_logits[t, topk_idx[t, j]] = topk_w[t, j] * (d_topk_w[t, j] - sum_i topk_w[t, i] * d_topk_w[t, i])

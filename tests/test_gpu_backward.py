@@ -135,3 +135,89 @@ def test_backward_rejects_unsupported_shapes():
     with pytest.raises(moe.MoeError) as e:
         moe.grouped_gemm_backward(x, perm, offsets, wgu, wdn, h, d_y, 2, 8, 0, 8)
     assert e.value.status == moe.MOE_EUNSUPPORTED
+
+
+# ----------------------------------------------------------------------------- kept pre-activations
+
+def _split_counts(counts):
+    return counts + [0] * (64 - len(counts))
+
+
+SAVED = [
+    (CASES[0], None), (CASES[2], None), (CASES[3], None), (CASES[4], None),
+    # one height class among 64 experts: every tile of both launches at half width
+    (mi.Workload("saved_split_over128", 3581, 320, 160, 64, 1, 0, 64, "bf16", 48),
+     [129, 255, 256, 257, 288, 289, 300, 350, 400, 513, 544]),
+    (mi.Workload("saved_split_to32", 80, 320, 160, 64, 1, 0, 64, "bf16", 49), [1, 16, 31, 32]),
+    (mi.Workload("saved_split_to128", 293, 320, 160, 64, 1, 0, 64, "bf16", 50), [65, 100, 128]),
+]
+
+
+@pytest.mark.parametrize("w,counts", SAVED, ids=[w.name for w, _ in SAVED])
+def test_saved_preactivations_match_recompute(w, counts):
+    """moe_grouped_gemm_gather_save writes the same h, y (and so out) as the plain
+    fused forward, and [G | U] matching the oracle's pre-activations; the backward
+    that reads them (moe_grouped_gemm_backward_saved) gives every gradient bit for
+    bit as the one that recomputes them."""
+    logits = mi.router_logits(w) if counts is None else _one_hot_logits(_split_counts(counts), w.E, w.seed)
+    if counts is not None:
+        assert int(sum(counts)) == w.T
+    x = mi.hidden_states(w)
+    wgu, wdn = mi.expert_weights(w)
+    d_out = g.to_dev(_d_out(w), "bf16")
+    print(f"case {w}", flush=True)
+    dx, dl = g.to_dev(x, "bf16"), g.to_dev(logits, "f32")
+    dgu, ddn = g.to_dev(wgu, "bf16"), g.to_dev(wdn, "bf16")
+    plain = moe.layer(dx, dl, dgu, ddn, w.k, w.e_begin, w.e_end, fused=True)
+    kept = moe.layer(dx, dl, dgu, ddn, w.k, w.e_begin, w.e_end, fused=True, save=True)
+    b_plain = moe.layer_backward(dx, dgu, ddn, plain, d_out, w.k, w.e_begin, w.e_end)
+    b_kept = moe.layer_backward(dx, dgu, ddn, kept, d_out, w.k, w.e_begin, w.e_end)
+    torch.cuda.synchronize()
+    n_loc = int(plain["offsets"][w.e_end] - plain["offsets"][w.e_begin])
+    for key in ("h", "y"):
+        assert torch.equal(kept[key][:n_loc].view(torch.int16), plain[key][:n_loc].view(torch.int16)), key
+    assert torch.equal(kept["out"].view(torch.int16), plain["out"].view(torch.int16))
+    # [G | U] against the oracle's gate/up product of the same rows
+    ref = oracle.moe_layer(mi.to_f64(x, "bf16"), logits, w.k, w.e_begin, w.e_end, mi.to_f64(wgu, "bf16"),
+                           mi.to_f64(wdn, "bf16"))
+    offs = ref["offsets"]
+    base = offs[w.e_begin]
+    gu_gpu = g.to_f64(kept["gu"][:n_loc])
+    gu_ref = np.zeros_like(gu_gpu)
+    wgu64 = mi.to_f64(wgu, "bf16")
+    for e in range(w.e_begin, w.e_end):
+        r0, r1 = offs[e] - base, offs[e + 1] - base
+        if r1 > r0:
+            gu_ref[r0:r1] = ref["x_perm"][r0:r1] @ wgu64[e - w.e_begin]
+    if n_loc:
+        assert g.rel_err(gu_gpu, gu_ref) <= TOL
+    for key in ("d_y", "d_w", "d_x_perm", "d_w_gate_up", "d_w_down", "d_x", "d_logits"):
+        a, b = b_kept[key], b_plain[key]
+        if key in ("d_y", "d_x_perm"):  # rows [0, N_loc) are written, the rest left as they were
+            a, b = a[:n_loc], b[:n_loc]
+        if a.dtype == torch.bfloat16:
+            a, b = a.view(torch.int16), b.view(torch.int16)
+        assert torch.equal(a, b), key
+
+
+def test_saved_entry_points_reject_a_missing_buffer():
+    w = CASES[0]
+    x = torch.zeros((w.T, w.d), dtype=torch.bfloat16, device="cuda")
+    perm = torch.zeros(w.T * w.k, dtype=torch.int32, device="cuda")
+    offsets = torch.zeros(w.E + 1, dtype=torch.int32, device="cuda")
+    wgu = torch.zeros((w.E_loc, w.d, 2 * w.d_ff), dtype=torch.bfloat16, device="cuda")
+    wdn = torch.zeros((w.E_loc, w.d_ff, w.d), dtype=torch.bfloat16, device="cuda")
+    n_max = w.T * min(w.k, w.E_loc)
+    h = torch.empty((n_max, w.d_ff), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((n_max, w.d), dtype=torch.bfloat16, device="cuda")
+    s = moe.shape(w.T, w.d, w.d_ff, w.E, w.k, w.e_begin, w.e_end)
+    import ctypes
+    lib = moe.lib()
+    st = lib.moe_grouped_gemm_gather_save(ctypes.byref(s), moe.MOE_BF16, x.data_ptr(), perm.data_ptr(),
+                                          offsets.data_ptr(), wgu.data_ptr(), wdn.data_ptr(), h.data_ptr(),
+                                          y.data_ptr(), None, None, None)
+    assert st == moe.MOE_EINVAL
+    st = lib.moe_grouped_gemm_backward_saved(ctypes.byref(s), moe.MOE_BF16, x.data_ptr(), perm.data_ptr(),
+                                             offsets.data_ptr(), wgu.data_ptr(), wdn.data_ptr(), h.data_ptr(), None,
+                                             y.data_ptr(), y.data_ptr(), wgu.data_ptr(), wdn.data_ptr(), None, None)
+    assert st == moe.MOE_EINVAL

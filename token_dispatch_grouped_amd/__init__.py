@@ -68,6 +68,9 @@ def _load():
             "moe_grouped_gemm_backward": (ctypes.c_int, [S, ctypes.c_int, P, P, P, P, P, P, P, P, P, P, P, P]),
             "moe_dispatch_backward": (ctypes.c_int, [S, ctypes.c_int, P, P, P, P]),
             "moe_route_topk_backward": (ctypes.c_int, [S, P, P, P, P, P]),
+            "moe_grouped_gemm_gather_save": (ctypes.c_int, [S, ctypes.c_int, P, P, P, P, P, P, P, P, P, P]),
+            "moe_grouped_gemm_backward_saved": (ctypes.c_int,
+                                                [S, ctypes.c_int, P, P, P, P, P, P, P, P, P, P, P, P, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(lib, name)
@@ -247,10 +250,11 @@ def grouped_gemm(x_perm, offsets, w_gate_up, w_down, T: int, k: int, E: int, e_b
 
 
 def grouped_gemm_gather(x, perm, offsets, w_gate_up, w_down, k: int, E: int, e_begin: int, e_end: int,
-                        h=None, y=None, stream=None):
+                        h=None, y=None, stream=None, gu=None):
     """grouped_gemm reading each local row straight from x through perm (no
     x_perm): returns (h [N_max, d_ff], y [N_max, d]), bit-identical to
-    dispatch + grouped_gemm."""
+    dispatch + grouped_gemm. With gu (a [N_max, 2*d_ff] tensor) the gate/up
+    pre-activations are kept there as well (moe_grouped_gemm_gather_save)."""
     torch = _torch()
     _dev(x, perm, offsets, w_gate_up, w_down)
     T, d = x.shape
@@ -269,9 +273,17 @@ def grouped_gemm_gather(x, perm, offsets, w_gate_up, w_down, k: int, E: int, e_b
     dt = _dtype_code(x)
     ws_bytes = _load().moe_grouped_gemm_workspace_bytes(ctypes.byref(s), dt)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device) if ws_bytes else None
-    _check(_load().moe_grouped_gemm_gather(ctypes.byref(s), dt, _ptr(x), _ptr(perm), _ptr(offsets),
-                                           _ptr(w_gate_up), _ptr(w_down), _ptr(h), _ptr(y), _ptr(ws),
-                                           _stream(stream)), "moe_grouped_gemm_gather")
+    if gu is None:
+        _check(_load().moe_grouped_gemm_gather(ctypes.byref(s), dt, _ptr(x), _ptr(perm), _ptr(offsets),
+                                               _ptr(w_gate_up), _ptr(w_down), _ptr(h), _ptr(y), _ptr(ws),
+                                               _stream(stream)), "moe_grouped_gemm_gather")
+    else:
+        _dev(gu)
+        if tuple(gu.shape) != (n_max, 2 * d_ff) or gu.dtype != x.dtype:
+            raise ValueError("gu must be [N_max, 2*d_ff] in the activations' dtype")
+        _check(_load().moe_grouped_gemm_gather_save(ctypes.byref(s), dt, _ptr(x), _ptr(perm), _ptr(offsets),
+                                                    _ptr(w_gate_up), _ptr(w_down), _ptr(h), _ptr(y), _ptr(gu),
+                                                    _ptr(ws), _stream(stream)), "moe_grouped_gemm_gather_save")
     return h, y
 
 
@@ -289,21 +301,31 @@ def combine(y, pair_pos, topk_w, T: int, k: int, E: int, e_begin: int, e_end: in
     return out
 
 
-def layer(x, logits, w_gate_up, w_down, k: int, e_begin: int, e_end: int, stream=None, fused: bool = False) -> dict:
+def layer(x, logits, w_gate_up, w_down, k: int, e_begin: int, e_end: int, stream=None, fused: bool = False,
+          save: bool = False) -> dict:
     """The whole forward of one rank: route -> dispatch -> grouped GEMM -> combine.
-    With `fused`, the dispatch writes indices only and the GEMM gathers the rows."""
+    With `fused`, the dispatch writes indices only and the GEMM gathers the rows.
+    With `save` (fused path), the gate/up pre-activations are kept in the result
+    as "gu", for layer_backward to use instead of recomputing them."""
+    torch = _torch()
     T = x.shape[0]
     E = logits.shape[1]
+    if save and not fused:
+        raise ValueError("save needs the fused path")
     idx, w = route_topk(logits, k, stream=stream)
     disp = dispatch(x, idx, E, e_begin, e_end, stream=stream, gather=not fused)
+    gu = None
     if fused:
+        if save:
+            e_loc, d_ff = w_down.shape[0], w_down.shape[1]
+            gu = torch.empty((T * min(k, e_loc), 2 * d_ff), dtype=x.dtype, device=x.device)
         h, y = grouped_gemm_gather(x, disp.perm, disp.offsets, w_gate_up, w_down, k, E, e_begin, e_end,
-                                   stream=stream)
+                                   stream=stream, gu=gu)
     else:
         h, y = grouped_gemm(disp.x_perm, disp.offsets, w_gate_up, w_down, T, k, E, e_begin, e_end, stream=stream)
     out = combine(y, disp.pair_pos, w, T, k, E, e_begin, e_end, stream=stream)
     return dict(idx=idx, w=w, counts=disp.counts, offsets=disp.offsets, perm=disp.perm,
-                pair_pos=disp.pair_pos, x_perm=disp.x_perm, h=h, y=y, out=out)
+                pair_pos=disp.pair_pos, x_perm=disp.x_perm, h=h, y=y, out=out, gu=gu)
 
 
 # ----------------------------------------------------------------------------- backward
@@ -331,8 +353,10 @@ def grouped_gemm_backward_workspace_bytes(T: int, d: int, d_ff: int, E: int, k: 
 
 
 def grouped_gemm_backward(x, perm, offsets, w_gate_up, w_down, h, d_y, k: int, E: int, e_begin: int, e_end: int,
-                          d_x_perm=None, d_w_gate_up=None, d_w_down=None, workspace=None, stream=None):
-    """(d_x_perm, d_w_gate_up, d_w_down): the gradient of the grouped expert FFN."""
+                          d_x_perm=None, d_w_gate_up=None, d_w_down=None, workspace=None, stream=None, gu=None):
+    """(d_x_perm, d_w_gate_up, d_w_down): the gradient of the grouped expert FFN.
+    With gu (the pre-activations the saving forward kept) they are not
+    recomputed (moe_grouped_gemm_backward_saved)."""
     torch = _torch()
     _dev(x, perm, offsets, w_gate_up, w_down, h, d_y)
     T, d = x.shape
@@ -349,10 +373,19 @@ def grouped_gemm_backward(x, perm, offsets, w_gate_up, w_down, h, d_y, k: int, E
     if ws is None:
         ws_bytes = _load().moe_grouped_gemm_backward_workspace_bytes(ctypes.byref(s), dt)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device) if ws_bytes else None
-    _check(_load().moe_grouped_gemm_backward(ctypes.byref(s), dt, _ptr(x), _ptr(perm), _ptr(offsets),
-                                             _ptr(w_gate_up), _ptr(w_down), _ptr(h), _ptr(d_y), _ptr(d_x_perm),
-                                             _ptr(d_w_gate_up), _ptr(d_w_down), _ptr(ws), _stream(stream)),
-           "moe_grouped_gemm_backward")
+    if gu is None:
+        _check(_load().moe_grouped_gemm_backward(ctypes.byref(s), dt, _ptr(x), _ptr(perm), _ptr(offsets),
+                                                 _ptr(w_gate_up), _ptr(w_down), _ptr(h), _ptr(d_y), _ptr(d_x_perm),
+                                                 _ptr(d_w_gate_up), _ptr(d_w_down), _ptr(ws), _stream(stream)),
+               "moe_grouped_gemm_backward")
+    else:
+        _dev(gu)
+        if tuple(gu.shape) != (h.shape[0], 2 * d_ff) or gu.dtype != h.dtype:
+            raise ValueError("gu must be [N_max, 2*d_ff] in the activations' dtype")
+        _check(_load().moe_grouped_gemm_backward_saved(ctypes.byref(s), dt, _ptr(x), _ptr(perm), _ptr(offsets),
+                                                       _ptr(w_gate_up), _ptr(w_down), _ptr(h), _ptr(gu), _ptr(d_y),
+                                                       _ptr(d_x_perm), _ptr(d_w_gate_up), _ptr(d_w_down), _ptr(ws),
+                                                       _stream(stream)), "moe_grouped_gemm_backward_saved")
     return d_x_perm, d_w_gate_up, d_w_down
 
 
@@ -384,12 +417,13 @@ def route_topk_backward(topk_idx, topk_w, d_topk_w, E: int, d_logits=None, strea
 
 def layer_backward(x, w_gate_up, w_down, fwd: dict, d_out, k: int, e_begin: int, e_end: int, stream=None) -> dict:
     """The whole backward of one rank, given the forward's dict (from layer()):
-    combine -> experts -> row gather -> router softmax."""
+    combine -> experts -> row gather -> router softmax. The gate/up
+    pre-activations come from the forward's "gu" when it kept them."""
     T = x.shape[0]
     E = fwd["counts"].shape[0]
     d_y, d_w = combine_backward(d_out, fwd["y"], fwd["pair_pos"], fwd["w"], T, k, E, e_begin, e_end, stream=stream)
     d_x_perm, d_wgu, d_wdn = grouped_gemm_backward(x, fwd["perm"], fwd["offsets"], w_gate_up, w_down, fwd["h"], d_y,
-                                                   k, E, e_begin, e_end, stream=stream)
+                                                   k, E, e_begin, e_end, stream=stream, gu=fwd.get("gu"))
     d_x = dispatch_backward(d_x_perm, fwd["pair_pos"], T, k, E, e_begin, e_end, stream=stream)
     d_logits = route_topk_backward(fwd["idx"], fwd["w"], d_w, E, stream=stream)
     return dict(d_y=d_y, d_w=d_w, d_x_perm=d_x_perm, d_w_gate_up=d_wgu, d_w_down=d_wdn, d_x=d_x, d_logits=d_logits)

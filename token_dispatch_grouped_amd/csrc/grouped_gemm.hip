@@ -323,8 +323,8 @@ hipError_t launch_grouped_gemm_bf16(const void* x_perm, const int32_t* offsets, 
   const char* force = getenv("MOE_GEMM_KERNEL");
   const bool regs = force != nullptr && strcmp(force, "regs") == 0;
   if (!regs && d % 32 == 0 && d_ff % 32 == 0)
-    return launch_grouped_gemm_lds(x_perm, nullptr, T, k, offsets, w_gu, w_dn, h, y, d, d_ff, e_begin, e_loc,
-                                   n_max, g1, g2, stream);
+    return launch_grouped_gemm_lds(x_perm, nullptr, T, k, offsets, w_gu, w_dn, h, y, nullptr, d, d_ff, e_begin,
+                                   e_loc, n_max, g1, g2, stream);
   hipLaunchKernelGGL(grouped_gemm_bf16_kernel<true>, dim3(g1), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(x_perm), static_cast<const uint16_t*>(w_gu),
                      static_cast<uint16_t*>(h), offsets, e_begin, e_loc, d, d_ff, 2 * d_ff,
@@ -337,14 +337,14 @@ hipError_t launch_grouped_gemm_bf16(const void* x_perm, const int32_t* offsets, 
 }
 
 hipError_t launch_grouped_gemm_gather(const void* x, const int32_t* perm, const int32_t* offsets,
-                                      const void* w_gu, const void* w_dn, void* h, void* y, int d, int d_ff,
-                                      int e_begin, int e_loc, int64_t n_max, int64_t T, int k,
+                                      const void* w_gu, const void* w_dn, void* h, void* y, void* gu, int d,
+                                      int d_ff, int e_begin, int e_loc, int64_t n_max, int64_t T, int k,
                                       hipStream_t stream) {
   if (n_max == 0) return hipSuccess;
   const int g1 = grid_for(n_max, e_loc, kBM, (d_ff + 127) / 128, 1);
   const int g2 = grid_for(n_max, e_loc, kBM, (d + 255) / 256, 1);
-  return launch_grouped_gemm_lds(x, perm, T, k, offsets, w_gu, w_dn, h, y, d, d_ff, e_begin, e_loc, n_max, g1, g2,
-                                 stream);
+  return launch_grouped_gemm_lds(x, perm, T, k, offsets, w_gu, w_dn, h, y, gu, d, d_ff, e_begin, e_loc, n_max, g1,
+                                 g2, stream);
 }
 
 hipError_t launch_grouped_gemm_f32(const float* x_perm, const int32_t* offsets, const float* w_gu,

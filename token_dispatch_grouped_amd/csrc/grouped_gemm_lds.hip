@@ -92,11 +92,12 @@ struct ARows {
   uint32_t a_bytes;         // bytes of A (T * K * 2)
 };
 
-template <bool SWIGLU, bool GATHER, int H, int BN>
+template <bool SWIGLU, bool GATHER, bool SAVE, int H, int BN>
 __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __restrict__ A,
                                           const uint16_t* __restrict__ Bexp, uint16_t* __restrict__ C,
-                                          int row0, int rows_valid, int n0, int K, int N, int ldb,
-                                          const ARows& ar) {
+                                          uint16_t* __restrict__ GU, int row0, int rows_valid, int n0, int K, int N,
+                                          int ldb, const ARows& ar) {
+  static_assert(!SAVE || SWIGLU, "pre-activations are kept only by the gate/up product");
   using L = Layout<H, BN>;
   constexpr int MI = L::MI, NI = L::NI, WM = L::WM, WN = L::WN, PER = L::PER;
   // A half-width tile does half the MFMA work per stage, so the same lookahead
@@ -448,30 +449,60 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
       }
     }
   }
+  if constexpr (SAVE) {
+    // The pre-activations too, for a backward that does not recompute them: every
+    // accumulator block goes to GU [rows][2 N] (gate columns first, then up), at
+    // the column its weight block came from, each wave storing its own blocks.
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(
+        GU + static_cast<int64_t>(row0) * 2 * N, static_cast<uint32_t>(rows_valid) * static_cast<uint32_t>(N) * 4u);
+    const uint32_t g_row_bytes = static_cast<uint32_t>(N) * 4u;
+    auto gu_off = [&](int slot) -> uint32_t {
+      const int bc = bcol(slot);
+      const int c = n0 + (bc < BN / 2 ? bc : bc - BN / 2) + l31;  // column inside the gate (or up) half
+      return c < N ? static_cast<uint32_t>(bc < BN / 2 ? c : N + c) * 2u : 0x80000000u;
+    };
+    auto save = [&](const f32x16_t& a, int row_base, uint32_t goff) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        __builtin_amdgcn_raw_buffer_store_b16(
+            f32_to_bf16_rne(a[r]), rg,
+            static_cast<int>(static_cast<uint32_t>(row_base + acc_row(r)) * g_row_bytes + goff), 0, 0);
+    };
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const uint32_t goff = gu_off(ni);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) save(acc[mi][ni], wm * (MI * 32) + mi * 32, goff);
+    }
+#pragma unroll
+    for (int x = 0; x < L::MX; ++x) save(acc_x[x], WM * MI * 32, gu_off(x == 0 ? 0 : X1));
+  }
 }
 
 // The tile height for rows_valid rows (a last row tile is the smallest that covers them).
-template <bool SWIGLU, bool GATHER, int BN>
+template <bool SWIGLU, bool GATHER, bool SAVE, int BN>
 __device__ __forceinline__ void run_tile(uint16_t* smem, const uint16_t* __restrict__ A,
-                                         const uint16_t* __restrict__ Bexp, uint16_t* __restrict__ C, int row0,
-                                         int rows_valid, int n0, int K, int N, int ldb, const ARows& ar) {
+                                         const uint16_t* __restrict__ Bexp, uint16_t* __restrict__ C,
+                                         uint16_t* __restrict__ GU, int row0, int rows_valid, int n0, int K, int N,
+                                         int ldb, const ARows& ar) {
   if (rows_valid > 256)
-    gemm_tile<SWIGLU, GATHER, 288, BN>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb, ar);
+    gemm_tile<SWIGLU, GATHER, SAVE, 288, BN>(smem, A, Bexp, C, GU, row0, rows_valid, n0, K, N, ldb, ar);
   else if (rows_valid > 128)
-    gemm_tile<SWIGLU, GATHER, 256, BN>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb, ar);
+    gemm_tile<SWIGLU, GATHER, SAVE, 256, BN>(smem, A, Bexp, C, GU, row0, rows_valid, n0, K, N, ldb, ar);
   else if (rows_valid > 64)
-    gemm_tile<SWIGLU, GATHER, 128, BN>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb, ar);
+    gemm_tile<SWIGLU, GATHER, SAVE, 128, BN>(smem, A, Bexp, C, GU, row0, rows_valid, n0, K, N, ldb, ar);
   else if (rows_valid > 32)
-    gemm_tile<SWIGLU, GATHER, 64, BN>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb, ar);
+    gemm_tile<SWIGLU, GATHER, SAVE, 64, BN>(smem, A, Bexp, C, GU, row0, rows_valid, n0, K, N, ldb, ar);
   else
-    gemm_tile<SWIGLU, GATHER, 32, BN>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb, ar);
+    gemm_tile<SWIGLU, GATHER, SAVE, 32, BN>(smem, A, Bexp, C, GU, row0, rows_valid, n0, K, N, ldb, ar);
 }
 
-template <bool SWIGLU, bool GATHER>
+// SAVE: the gate/up launch also writes its pre-activations [G | U] to GU.
+template <bool SWIGLU, bool GATHER, bool SAVE>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_lds_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
-    const int32_t* __restrict__ offsets, int e_begin, int e_loc, int K, int N, int ldb, int n_max,
-    const int32_t* __restrict__ perm, int k, uint32_t a_bytes) {
+    uint16_t* __restrict__ GU, const int32_t* __restrict__ offsets, int e_begin, int e_loc, int K, int N, int ldb,
+    int n_max, const int32_t* __restrict__ perm, int k, uint32_t a_bytes) {
   __shared__ __attribute__((aligned(1024))) uint16_t smem[kStages * (kAStageElems + kBStageElems)];
   __shared__ SortedTileMap tm;
   // a remainder of at most 32 rows rides on the expert's last full tile (288 rows)
@@ -517,9 +548,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_lds_kernel(
     const bool half = part != 0 || (narrow_last && tc.nt == n_tiles - 1 && rows_valid > 32);
     const uint16_t* Bexp = B + static_cast<int64_t>(tc.e) * b_expert;
     if (half)
-      run_tile<SWIGLU, GATHER, 128>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb, ar);
+      run_tile<SWIGLU, GATHER, SAVE, 128>(smem, A, Bexp, C, GU, row0, rows_valid, n0, K, N, ldb, ar);
     else
-      run_tile<SWIGLU, GATHER, 256>(smem, A, Bexp, C, row0, rows_valid, n0, K, N, ldb, ar);
+      run_tile<SWIGLU, GATHER, SAVE, 256>(smem, A, Bexp, C, GU, row0, rows_valid, n0, K, N, ldb, ar);
     // every wave has waited for its last LDS reads; the next tile's loads may land
     __builtin_amdgcn_s_barrier();
   }
@@ -528,33 +559,40 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_lds_kernel(
 }  // namespace
 
 hipError_t launch_grouped_gemm_lds(const void* a, const int32_t* perm, int64_t T, int k, const int32_t* offsets,
-                                   const void* w_gu, const void* w_dn, void* h, void* y, int d, int d_ff,
+                                   const void* w_gu, const void* w_dn, void* h, void* y, void* gu, int d, int d_ff,
                                    int e_begin, int e_loc, int64_t n_max, int grid_gate_up, int grid_down,
                                    hipStream_t stream) {
+  const uint16_t* wgu = static_cast<const uint16_t*>(w_gu);
+  uint16_t* hh = static_cast<uint16_t*>(h);
+  uint16_t* g = static_cast<uint16_t*>(gu);
   if (perm != nullptr) {  // activation rows gathered from x by perm
     const uint32_t a_bytes = static_cast<uint32_t>(T * d * 2);
-    hipLaunchKernelGGL((grouped_gemm_lds_kernel<true, true>), dim3(grid_gate_up), dim3(kThreads), 0, stream,
-                       static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(w_gu),
-                       static_cast<uint16_t*>(h), offsets, e_begin, e_loc, d, d_ff, 2 * d_ff,
-                       static_cast<int>(n_max), perm, k, a_bytes);
+    const uint16_t* x = static_cast<const uint16_t*>(a);
+    if (gu != nullptr)
+      hipLaunchKernelGGL((grouped_gemm_lds_kernel<true, true, true>), dim3(grid_gate_up), dim3(kThreads), 0, stream,
+                         x, wgu, hh, g, offsets, e_begin, e_loc, d, d_ff, 2 * d_ff, static_cast<int>(n_max), perm, k,
+                         a_bytes);
+    else
+      hipLaunchKernelGGL((grouped_gemm_lds_kernel<true, true, false>), dim3(grid_gate_up), dim3(kThreads), 0, stream,
+                         x, wgu, hh, nullptr, offsets, e_begin, e_loc, d, d_ff, 2 * d_ff, static_cast<int>(n_max),
+                         perm, k, a_bytes);
   } else {
-    hipLaunchKernelGGL((grouped_gemm_lds_kernel<true, false>), dim3(grid_gate_up), dim3(kThreads), 0, stream,
-                       static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(w_gu),
-                       static_cast<uint16_t*>(h), offsets, e_begin, e_loc, d, d_ff, 2 * d_ff,
+    hipLaunchKernelGGL((grouped_gemm_lds_kernel<true, false, false>), dim3(grid_gate_up), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(a), wgu, hh, nullptr, offsets, e_begin, e_loc, d, d_ff, 2 * d_ff,
                        static_cast<int>(n_max), nullptr, k, 0u);
   }
-  hipLaunchKernelGGL((grouped_gemm_lds_kernel<false, false>), dim3(grid_down), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((grouped_gemm_lds_kernel<false, false, false>), dim3(grid_down), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_dn),
-                     static_cast<uint16_t*>(y), offsets, e_begin, e_loc, d_ff, d, d, static_cast<int>(n_max),
+                     static_cast<uint16_t*>(y), nullptr, offsets, e_begin, e_loc, d_ff, d, d, static_cast<int>(n_max),
                      nullptr, k, 0u);
   return hipGetLastError();
 }
 
 hipError_t launch_grouped_gemm_plain(const void* a, const void* b, void* c, const int32_t* offsets, int e_begin,
                                      int e_loc, int K, int N, int ldb, int64_t n_max, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((grouped_gemm_lds_kernel<false, false>), dim3(grid), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((grouped_gemm_lds_kernel<false, false, false>), dim3(grid), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), static_cast<uint16_t*>(c),
-                     offsets, e_begin, e_loc, K, N, ldb, static_cast<int>(n_max), nullptr, 1, 0u);
+                     nullptr, offsets, e_begin, e_loc, K, N, ldb, static_cast<int>(n_max), nullptr, 1, 0u);
   return hipGetLastError();
 }
 

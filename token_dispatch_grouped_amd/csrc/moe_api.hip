@@ -151,10 +151,13 @@ moe_status moe_grouped_gemm(const moe_shape* s, moe_dtype dt, const void* x_perm
       s->e_begin, e_loc, n_max, stream));
 }
 
-moe_status moe_grouped_gemm_gather(const moe_shape* s, moe_dtype dt, const void* x, const int32_t* perm,
-                                   const int32_t* offsets, const void* w_gate_up, const void* w_down, void* h,
-                                   void* y, void* workspace, hipStream_t stream) {
-  (void)workspace;
+}  // extern "C"
+
+namespace {
+
+// moe_grouped_gemm_gather, and with gu != nullptr moe_grouped_gemm_gather_save
+moe_status gemm_gather(const moe_shape* s, moe_dtype dt, const void* x, const int32_t* perm, const int32_t* offsets,
+                       const void* w_gate_up, const void* w_down, void* h, void* y, void* gu, hipStream_t stream) {
   const moe_status st = check_shape(s, true);
   if (st != MOE_OK) return st;
   if (!valid_dtype(dt)) return MOE_EINVAL;
@@ -169,9 +172,28 @@ moe_status moe_grouped_gemm_gather(const moe_shape* s, moe_dtype dt, const void*
   if ((static_cast<int64_t>(s->d) + 64) * 2 * s->d_ff * 2 > INT32_MAX ||
       (static_cast<int64_t>(s->d_ff) + 64) * s->d * 2 > INT32_MAX)
     return MOE_EUNSUPPORTED;
-  return from_hip(moe::launch_grouped_gemm_gather(x, perm, offsets, w_gate_up, w_down, h, y, s->d, s->d_ff,
+  return from_hip(moe::launch_grouped_gemm_gather(x, perm, offsets, w_gate_up, w_down, h, y, gu, s->d, s->d_ff,
                                                   s->e_begin, s->e_end - s->e_begin, n_max_of(s), s->T, s->k,
                                                   stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_grouped_gemm_gather(const moe_shape* s, moe_dtype dt, const void* x, const int32_t* perm,
+                                   const int32_t* offsets, const void* w_gate_up, const void* w_down, void* h,
+                                   void* y, void* workspace, hipStream_t stream) {
+  (void)workspace;
+  return gemm_gather(s, dt, x, perm, offsets, w_gate_up, w_down, h, y, nullptr, stream);
+}
+
+moe_status moe_grouped_gemm_gather_save(const moe_shape* s, moe_dtype dt, const void* x, const int32_t* perm,
+                                        const int32_t* offsets, const void* w_gate_up, const void* w_down, void* h,
+                                        void* y, void* gu, void* workspace, hipStream_t stream) {
+  (void)workspace;
+  if (s != nullptr && s->T > 0 && gu == nullptr) return MOE_EINVAL;
+  return gemm_gather(s, dt, x, perm, offsets, w_gate_up, w_down, h, y, gu, stream);
 }
 
 moe_status moe_combine(const moe_shape* s, moe_dtype dt, const void* y, const int32_t* pair_pos,
@@ -206,10 +228,16 @@ size_t moe_grouped_gemm_backward_workspace_bytes(const moe_shape* s, moe_dtype d
   return backward_ws(s, nullptr, nullptr);
 }
 
-moe_status moe_grouped_gemm_backward(const moe_shape* s, moe_dtype dt, const void* x, const int32_t* perm,
-                                     const int32_t* offsets, const void* w_gate_up, const void* w_down,
-                                     const void* h, const void* d_y, void* d_x_perm, void* d_w_gate_up,
-                                     void* d_w_down, void* workspace, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// moe_grouped_gemm_backward (saved == nullptr: [G | U] recomputed into the
+// workspace) and moe_grouped_gemm_backward_saved ([G | U] read from saved)
+moe_status gemm_backward(const moe_shape* s, moe_dtype dt, const void* x, const int32_t* perm,
+                         const int32_t* offsets, const void* w_gate_up, const void* w_down, const void* h,
+                         const void* saved, const void* d_y, void* d_x_perm, void* d_w_gate_up, void* d_w_down,
+                         void* workspace, hipStream_t stream) {
   const moe_status st = check_shape(s, true);
   if (st != MOE_OK) return st;
   if (!valid_dtype(dt)) return MOE_EINVAL;
@@ -235,16 +263,17 @@ moe_status moe_grouped_gemm_backward(const moe_shape* s, moe_dtype dt, const voi
   backward_ws(s, &off_gu, &off_dgu);
   char* ws = static_cast<char*>(workspace);
   void* x_perm = ws;
-  void* gu = ws + off_gu;
+  const void* gu = saved != nullptr ? saved : static_cast<const void*>(ws + off_gu);
   void* d_gu = ws + off_dgu;
   hipError_t e = hipSuccess;
   if (n_max > 0) {
-    // the rows of the local pairs, then their gate/up pre-activations (recomputed, not stored by the forward)
+    // the rows of the local pairs, then (unless the forward kept them) their gate/up pre-activations
     e = moe::launch_gather_rows(x, static_cast<size_t>(d) * 2, perm, offsets, x_perm, s->k, s->e_begin, s->e_end,
                                 n_max, stream);
-    if (e == hipSuccess)
-      e = moe::launch_grouped_gemm_plain(x_perm, w_gate_up, gu, offsets, s->e_begin, e_loc, d, 2 * d_ff, 2 * d_ff,
-                                         n_max, moe::grouped_gemm_grid(n_max, e_loc, (2 * d_ff + 255) / 256), stream);
+    if (e == hipSuccess && saved == nullptr)
+      e = moe::launch_grouped_gemm_plain(x_perm, w_gate_up, ws + off_gu, offsets, s->e_begin, e_loc, d, 2 * d_ff,
+                                         2 * d_ff, n_max,
+                                         moe::grouped_gemm_grid(n_max, e_loc, (2 * d_ff + 255) / 256), stream);
     // [dG | dU] from dH = dY @ W_dn^T and [G | U]
     if (e == hipSuccess)
       e = moe::launch_grouped_gemm_nt(d_y, w_down, d_gu, gu, offsets, s->e_begin, e_loc, d, d_ff, 2 * d_ff, n_max,
@@ -269,6 +298,27 @@ moe_status moe_grouped_gemm_backward(const moe_shape* s, moe_dtype dt, const voi
     e = moe::launch_grouped_gemm_tn(x_perm, d_gu, d_w_gate_up, offsets, s->e_begin, e_loc, d, 2 * d_ff, n_max,
                                     tn_grid(d, 2 * d_ff), stream);
   return from_hip(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_grouped_gemm_backward(const moe_shape* s, moe_dtype dt, const void* x, const int32_t* perm,
+                                     const int32_t* offsets, const void* w_gate_up, const void* w_down,
+                                     const void* h, const void* d_y, void* d_x_perm, void* d_w_gate_up,
+                                     void* d_w_down, void* workspace, hipStream_t stream) {
+  return gemm_backward(s, dt, x, perm, offsets, w_gate_up, w_down, h, nullptr, d_y, d_x_perm, d_w_gate_up, d_w_down,
+                       workspace, stream);
+}
+
+moe_status moe_grouped_gemm_backward_saved(const moe_shape* s, moe_dtype dt, const void* x, const int32_t* perm,
+                                           const int32_t* offsets, const void* w_gate_up, const void* w_down,
+                                           const void* h, const void* gu, const void* d_y, void* d_x_perm,
+                                           void* d_w_gate_up, void* d_w_down, void* workspace, hipStream_t stream) {
+  if (s != nullptr && s->T > 0 && gu == nullptr) return MOE_EINVAL;
+  return gemm_backward(s, dt, x, perm, offsets, w_gate_up, w_down, h, gu, d_y, d_x_perm, d_w_gate_up, d_w_down,
+                       workspace, stream);
 }
 
 moe_status moe_dispatch_backward(const moe_shape* s, moe_dtype dt, const void* d_x_perm, const int32_t* pair_pos,
