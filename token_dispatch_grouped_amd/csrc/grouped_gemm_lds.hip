@@ -364,6 +364,21 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
   };
   auto acc_row = [&](int r) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); };  // row of element r in a block
 
+  // SAVE: the pre-activations go to GU [rows][2 N] (gate columns, then the up
+  // columns) as they are read for H, at the output column of the pair: G at
+  // column c and U at column N + c of the row.
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(
+      SAVE ? GU + static_cast<int64_t>(row0) * 2 * N : GU,
+      SAVE ? static_cast<uint32_t>(rows_valid) * static_cast<uint32_t>(N) * 4u : 0u);
+  auto save = [&](float v, int row, uint32_t coff, bool up) {
+    if constexpr (SAVE) {
+      const uint32_t o = coff + (up ? c_row_bytes : 0u);  // an out-of-range coff stays out of range
+      __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(v), rg,
+                                            static_cast<int>(static_cast<uint32_t>(row) * 2u * c_row_bytes + o), 0,
+                                            0);
+    }
+  };
+
   // Where a gate block and its up block sit in different waves (one block per
   // wave; or the shared extra row block of a half-width 288-row tile), the up
   // wave hands its 16 accumulators per lane over through LDS, in the activation
@@ -395,11 +410,20 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
     }
   }
 
-  if constexpr (XCH_MAIN) {  // 32 rows: waves 0 and 1 write silu(gate) * up
+  if constexpr (XCH_MAIN) {  // 32 rows: waves 0 and 1 write silu(gate) * up, waves 2 and 3 keep their up
     if (wn < 2) {
       const uint32_t coff = col_off(0);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) store(silu_fast(acc[0][0][r]) * up_in[r], acc_row(r), coff);
+      for (int r = 0; r < 16; ++r) {
+        const float gv = acc[0][0][r];
+        store(silu_fast(gv) * up_in[r], acc_row(r), coff);
+        save(gv, acc_row(r), coff, false);
+      }
+    } else if constexpr (SAVE) {
+      const int c = n0 + (wn - 2) * 32 + l31;  // the output column of this up block
+      const uint32_t coff = c < N ? static_cast<uint32_t>(c) * 2u : 0x80000000u;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) save(acc[0][0][r], acc_row(r), coff, true);
     }
   } else if constexpr (SWIGLU && NI == 2 && L::XR) {
     // half-width 288-row tile: the second wave row holds its up block in slot 0
@@ -410,7 +434,11 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float a0 = acc[mi][0][r], a1 = acc[mi][1][r];
-        store(gs ? silu_fast(a1) * a0 : silu_fast(a0) * a1, wm * (MI * 32) + mi * 32 + acc_row(r), coff);
+        const float gv = gs ? a1 : a0, uv = gs ? a0 : a1;
+        const int row = wm * (MI * 32) + mi * 32 + acc_row(r);
+        store(silu_fast(gv) * uv, row, coff);
+        save(gv, row, coff, false);
+        save(uv, row, coff, true);
       }
   } else {
     constexpr int kStoreBlocks = SWIGLU ? NI / 2 : NI;
@@ -423,23 +451,42 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
       for (int r = 0; r < 16; ++r) {
         const int row = wm * (MI * 32) + mi * 32 + acc_row(r);
 #pragma unroll
-        for (int ni = 0; ni < kStoreBlocks; ++ni)
-          store(SWIGLU ? silu_fast(acc[mi][ni][r]) * acc[mi][ni + NI / 2][r] : acc[mi][ni][r], row, coff[ni]);
+        for (int ni = 0; ni < kStoreBlocks; ++ni) {
+          if constexpr (SWIGLU) {
+            const float gv = acc[mi][ni][r], uv = acc[mi][ni + NI / 2][r];
+            store(silu_fast(gv) * uv, row, coff[ni]);
+            save(gv, row, coff[ni], false);
+            save(uv, row, coff[ni], true);
+          } else {
+            store(acc[mi][ni][r], row, coff[ni]);
+          }
+        }
       }
     }
   }
   if constexpr (L::MX > 0) {  // the extra row block (rows WM * MI * 32 ...)
     const int row0x = WM * MI * 32;
     if constexpr (XCH_X) {  // gate half here in the first wave row, up half handed over by the second
+      const uint32_t coff = col_off(0);
       if (wm == 0) {
-        const uint32_t coff = col_off(0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) store(silu_fast(acc_x[0][r]) * up_in[r], row0x + acc_row(r), coff);
+        for (int r = 0; r < 16; ++r) {
+          store(silu_fast(acc_x[0][r]) * up_in[r], row0x + acc_row(r), coff);
+          save(acc_x[0][r], row0x + acc_row(r), coff, false);
+        }
+      } else if constexpr (SAVE) {  // slot 0 of the second wave row is the up block of the same columns
+        const uint32_t ucoff = col_off(1);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) save(acc_x[0][r], row0x + acc_row(r), ucoff, true);
       }
     } else if constexpr (SWIGLU) {  // slot 0 with its up pair X1
       const uint32_t coff = col_off(0);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) store(silu_fast(acc_x[0][r]) * acc_x[1][r], row0x + acc_row(r), coff);
+      for (int r = 0; r < 16; ++r) {
+        store(silu_fast(acc_x[0][r]) * acc_x[1][r], row0x + acc_row(r), coff);
+        save(acc_x[0][r], row0x + acc_row(r), coff, false);
+        save(acc_x[1][r], row0x + acc_row(r), coff, true);
+      }
     } else {  // slots 0 .. MX-1
 #pragma unroll
       for (int x = 0; x < L::MX; ++x) {
@@ -448,34 +495,6 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
         for (int r = 0; r < 16; ++r) store(acc_x[x][r], row0x + acc_row(r), coff);
       }
     }
-  }
-  if constexpr (SAVE) {
-    // The pre-activations too, for a backward that does not recompute them: every
-    // accumulator block goes to GU [rows][2 N] (gate columns first, then up), at
-    // the column its weight block came from, each wave storing its own blocks.
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(
-        GU + static_cast<int64_t>(row0) * 2 * N, static_cast<uint32_t>(rows_valid) * static_cast<uint32_t>(N) * 4u);
-    const uint32_t g_row_bytes = static_cast<uint32_t>(N) * 4u;
-    auto gu_off = [&](int slot) -> uint32_t {
-      const int bc = bcol(slot);
-      const int c = n0 + (bc < BN / 2 ? bc : bc - BN / 2) + l31;  // column inside the gate (or up) half
-      return c < N ? static_cast<uint32_t>(bc < BN / 2 ? c : N + c) * 2u : 0x80000000u;
-    };
-    auto save = [&](const f32x16_t& a, int row_base, uint32_t goff) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        __builtin_amdgcn_raw_buffer_store_b16(
-            f32_to_bf16_rne(a[r]), rg,
-            static_cast<int>(static_cast<uint32_t>(row_base + acc_row(r)) * g_row_bytes + goff), 0, 0);
-    };
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni) {
-      const uint32_t goff = gu_off(ni);
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) save(acc[mi][ni], wm * (MI * 32) + mi * 32, goff);
-    }
-#pragma unroll
-    for (int x = 0; x < L::MX; ++x) save(acc_x[x], WM * MI * 32, gu_off(x == 0 ? 0 : X1));
   }
 }
 
