@@ -34,8 +34,13 @@
 //     remainder gets its own tile of the smallest of 32/64/128/256 rows that
 //     covers it. Wave layouts: 2 x 2 waves of (H/2) x 128 for H >= 64, 1 x 4
 //     waves of 32 x 64 for H = 32.
-//   * Tile walk, XCD mapping and the buffer-store epilogue follow the
-//     register-staged kernel.
+//   * Half-width tiles (128 weight columns, five stages in the same LDS) for
+//     balance: the last round's tiles when they would fill at most half of the
+//     workgroups, and a last column block that is at most half full.
+//   * Tile walk: persistent workgroups, experts ordered by the height class of
+//     their tiles, rounds walked in snake order, each XCD given a contiguous
+//     range of tile ids (gemm_common.h). Epilogue: bf16 buffer stores bounded by
+//     the tile's valid rows; SAVE also keeps the gate/up pre-activations.
 #include <type_traits>
 
 #include "lds_pipe.h"
