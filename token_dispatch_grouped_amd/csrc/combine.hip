@@ -19,10 +19,6 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-#ifndef MOE_COMBINE_CHUNKS
-#define MOE_COMBINE_CHUNKS 8
-#endif
-constexpr int kChunks = MOE_COMBINE_CHUNKS;  // 16-byte chunks per lane per pass
 
 template <bool BF16>
 struct Vec;
@@ -63,7 +59,8 @@ struct Vec<false> {  // 4 fp32 per 16 bytes
   }
 };
 
-template <bool BF16, bool UNIT>
+// kChunks: 16-byte chunks per lane per pass over a row (a pass covers kChunks KB)
+template <bool BF16, bool UNIT, int kChunks>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const uint4* __restrict__ y,
                                                            const int32_t* __restrict__ pair_pos,
                                                            const float* __restrict__ w,
@@ -123,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint4* __restri
           for (int q = 0; q < kChunks; ++q) v0[q] = buffer_load16(b0, static_cast<uint32_t>(q * kWave + lane) * 16u);
 #pragma unroll
           for (int q = 0; q < kChunks; ++q) v1[q] = buffer_load16(b1, static_cast<uint32_t>(q * kWave + lane) * 16u);
-          __builtin_amdgcn_sched_barrier(0);  // all eight loads in flight before the first use
+          __builtin_amdgcn_sched_barrier(0);  // both rows' loads in flight before the first use
 #pragma unroll
           for (int q = 0; q < kChunks; ++q) {
             float f[V::kN];
@@ -161,17 +158,28 @@ hipError_t launch_combine(const void* y, const int32_t* pair_pos, const float* w
   const int row_vec = bf16 ? d / 8 : d / 4;
   int64_t blocks = (T + (kThreads / kWave) - 1) / (kThreads / kWave);
   if (blocks > 4096) blocks = 4096;
-#define MOE_COMBINE_LAUNCH(B, U)                                                                         \
-  hipLaunchKernelGGL((combine_kernel<B, U>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, \
+  // Chunks per lane and pass, by row length (measured, one box, timing each in the
+  // layer): rows of more than 8 KB take 8 (skew256's 14 KB rows: 45 us, against
+  // 49 with 4 and 56 with 2); 6-8 KB rows take 4 (dense8: 18.7 us against 20.2
+  // with 8); shorter rows take 2 (ep8_share128's 5.6 KB: 15.7 us against 17.5):
+  // fewer registers, so more of the token waves are resident at once.
+  const int chunks = row_vec > 512 ? 8 : row_vec > 384 ? 4 : 2;
+#define MOE_COMBINE_LAUNCH(B, U, C)                                                                          \
+  hipLaunchKernelGGL((combine_kernel<B, U, C>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, \
                      static_cast<const uint4*>(y), pair_pos, w, static_cast<uint4*>(out), T, k, row_vec, n_max)
+#define MOE_COMBINE_CHUNKS(B, U)            \
+  if (chunks == 8) MOE_COMBINE_LAUNCH(B, U, 8); \
+  else if (chunks == 4) MOE_COMBINE_LAUNCH(B, U, 4); \
+  else MOE_COMBINE_LAUNCH(B, U, 2)
   // w == nullptr: every local pair has weight 1 (the gradient of the row gather)
   if (bf16) {
-    if (w) MOE_COMBINE_LAUNCH(true, false);
-    else MOE_COMBINE_LAUNCH(true, true);
+    if (w) MOE_COMBINE_CHUNKS(true, false);
+    else MOE_COMBINE_CHUNKS(true, true);
   } else {
-    if (w) MOE_COMBINE_LAUNCH(false, false);
-    else MOE_COMBINE_LAUNCH(false, true);
+    if (w) MOE_COMBINE_CHUNKS(false, false);
+    else MOE_COMBINE_CHUNKS(false, true);
   }
+#undef MOE_COMBINE_CHUNKS
 #undef MOE_COMBINE_LAUNCH
   return hipGetLastError();
 }
