@@ -288,10 +288,12 @@ __global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(
   }
 }
 
-// Rows are copied in parts of kGatherVec 16-byte vectors (8 per lane), one part
-// per wave, so that a few long rows still spread over many waves and every lane
-// keeps 8 loads in flight.
-constexpr int kGatherPerLane = 8;
+// Rows are copied in parts of kGatherVec 16-byte vectors (2 per lane), one part
+// per wave at a time, so that a few long rows still spread over many waves. Two
+// per lane, with more parts and waves, measured faster than 4 or 8 on every
+// workload (dense8 21.0 us against 21.5 with 8, skew256 15.0 against 16.7,
+// ep8_share128 10.0 against 11.2).
+constexpr int kGatherPerLane = 2;
 constexpr int kGatherVec = kWave * kGatherPerLane;
 
 __global__ __launch_bounds__(kThreads) void dispatch_gather_kernel(
