@@ -43,6 +43,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "gemm_common.h"
 
 namespace moe {
@@ -279,17 +281,19 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_f32_kernel(
   }
 }
 
+// CU count of the current device, queried once per device. Atomic, so that
+// callers launching from several host threads at once read and fill it safely.
 int device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 // Persistent grid: enough workgroups to fill the chip, never more than the
