@@ -405,3 +405,43 @@ def test_dispatch_both_chunk_sizes(T, k, E, lo, hi):
     pair_pos = np.full(T * k, -1)
     pair_pos[perm[seg0:seg1]] = np.arange(seg1 - seg0)
     np.testing.assert_array_equal(disp.pair_pos.cpu().numpy(), pair_pos)
+
+
+def test_layers_on_two_streams_from_two_threads():
+    """The library keeps no state between calls, so two host threads, each running
+    a different layer on its own stream at the same time, get the results of the
+    same layers run one after the other, bit for bit."""
+    import threading
+
+    cases = [mi.Workload("stream_a", 900, 256, 256, 32, 4, 8, 12, "bf16", 51),
+             mi.Workload("stream_b", 1200, 320, 192, 8, 2, 0, 8, "bf16", 52)]
+    args = []
+    for w in cases:
+        args.append((g.to_dev(mi.hidden_states(w), "bf16"), g.to_dev(mi.router_logits(w), "f32"),
+                     *(g.to_dev(a, "bf16") for a in mi.expert_weights(w)), w.k, w.e_begin, w.e_end))
+    alone = []
+    for a in args:
+        alone.append(moe.layer(*a, fused=True)["out"])
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    got = [[], []]
+    errors = []
+
+    def run(i):
+        try:
+            with torch.cuda.stream(streams[i]):
+                for _ in range(3):
+                    got[i].append(moe.layer(*args[i], stream=streams[i], fused=True)["out"])
+        except Exception as e:  # pragma: no cover - reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(2):
+        for out in got[i]:
+            assert torch.equal(out.view(torch.int16), alone[i].view(torch.int16)), i
