@@ -91,28 +91,37 @@ __global__ __launch_bounds__(kThreads) void dispatch_bases_kernel(const int32_t*
   const int lane = lane_id();
   const int wv = threadIdx.x / kWave;
   if (wv == 0) {
-    int carry = 0;
-    for (int e0 = 0; e0 < E; e0 += kWave) {
-      const int e = e0 + lane;
-      const int v = e < E ? tot[e] : 0;
-      int incl = v;
+    // the <= 1024 totals: lane L scans the run of kTotRun experts from L * kTotRun
+    constexpr int kTotRun = (kMaxExperts + kWave - 1) / kWave;
+    const int e0 = lane * kTotRun;
+    int v[kTotRun];
 #pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const int o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-      }
-      if (e < E) {
-        off_s[e] = carry + incl - v;
+    for (int i = 0; i < kTotRun; ++i) v[i] = e0 + i < E ? tot[e0 + i] : 0;
+    int run = 0;
+#pragma unroll
+    for (int i = 0; i < kTotRun; ++i) run += v[i];
+    int incl = run;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    int off_e = incl - run;
+#pragma unroll
+    for (int i = 0; i < kTotRun; ++i) {
+      if (e0 + i < E) {
+        off_s[e0 + i] = off_e;
         if (blockIdx.x == 0) {
-          offsets[e] = carry + incl - v;
-          counts[e] = v;
+          offsets[e0 + i] = off_e;
+          counts[e0 + i] = v[i];
         }
       }
-      carry += __shfl(incl, kWave - 1);
+      off_e += v[i];
     }
+    const int all = __shfl(incl, kWave - 1);
     if (lane == 0) {
-      off_s[E] = carry;
-      if (blockIdx.x == 0) offsets[E] = carry;
+      off_s[E] = all;
+      if (blockIdx.x == 0) offsets[E] = all;
     }
   }
   __syncthreads();
@@ -120,16 +129,31 @@ __global__ __launch_bounds__(kThreads) void dispatch_bases_kernel(const int32_t*
   if (e >= E) return;
   const int32_t* row = ws + static_cast<int64_t>(e) * n_chunks;
   int carry = off_s[e];
-  for (int c0 = 0; c0 < n_chunks; c0 += kWave) {
-    const int c = c0 + lane;
-    const int v = c < n_chunks ? row[c] : 0;
-    int incl = v;
+  // Batches of 64 * kRun chunks: lane L takes the run of kRun consecutive chunks
+  // from L * kRun, loads them all before adding, sums its run, and one wave scan
+  // of the run sums places every run. A batch costs one load latency and one
+  // scan, where a chunk per lane and pass cost one of each per 64 chunks.
+  constexpr int kRun = 8;
+  for (int b0 = 0; b0 < n_chunks; b0 += kWave * kRun) {
+    const int c0 = b0 + lane * kRun;
+    int v[kRun];
+#pragma unroll
+    for (int i = 0; i < kRun; ++i) v[i] = c0 + i < n_chunks ? row[c0 + i] : 0;
+    int run = 0;
+#pragma unroll
+    for (int i = 0; i < kRun; ++i) run += v[i];
+    int incl = run;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
       const int o = __shfl_up(incl, off);
       if (lane >= off) incl += o;
     }
-    if (c < n_chunks) base[static_cast<int64_t>(c) * E + e] = carry + incl - v;
+    int slot = carry + incl - run;  // first sorted slot of chunk c0 for expert e
+#pragma unroll
+    for (int i = 0; i < kRun; ++i) {
+      if (c0 + i < n_chunks) base[static_cast<int64_t>(c0 + i) * E + e] = slot;
+      slot += v[i];
+    }
     carry += __shfl(incl, kWave - 1);
   }
 }
