@@ -4,9 +4,18 @@ A step is the whole path on one batch already resident in HBM: route top-k ->
 dispatch -> grouped GEMM (gate/up + SwiGLU, then down) -> combine, through the
 C ABI, with every buffer allocated before timing. Prints ONE JSON line.
 
+Timing: W warm-up steps, then K timed steps, each bracketed by events on the
+stream the kernels run on, with a write of at least 512 MiB to a scratch buffer
+before each step and outside its events, so the 4 MB L2s and the 256 MB
+Infinity Cache hold none of the step's inputs when it starts. The K steps are
+bracketed by a device synchronisation on both sides; `value` and `ms_per_step`
+use the median of the per-step event times. The same K steps back to back, with
+no flush, give `back_to_back_ms_per_step` (wall clock) for comparison.
+
 The roofline object covers the grouped GEMM (both of its MFMA launches), timed
-with events recorded on the stream the kernels run on. The CPU baseline is the
-fp64 oracle on a bounded sample of the same workload, timed on the host cores.
+with events around it inside every timed step (median). The CPU baseline is
+the fp64 oracle on a bounded sample of the same workload, timed on the host
+cores.
 """
 from __future__ import annotations
 
@@ -106,6 +115,24 @@ def sample_sclk(step, seconds: float, torch):
     return float(np.median(samples)) if samples else None
 
 
+def sha256_of(a: np.ndarray) -> str:
+    return hashlib.sha256(np.ascontiguousarray(a).view(np.uint8)).hexdigest()
+
+
+def versions(torch) -> dict:
+    v = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
+    try:
+        with open("/opt/rocm/.info/version") as fh:
+            v["rocm"] = fh.read().strip()
+    except OSError:
+        v["rocm"] = None
+    try:
+        v["device"] = torch.cuda.get_device_properties(0).gcnArchName
+    except (AttributeError, RuntimeError):
+        v["device"] = None
+    return v
+
+
 def cpu_baseline(w: mi.Workload, logits, x, wgu, wdn, budget_s: float = 12.0) -> dict:
     """The oracle, as it stands, on the first T_s tokens of the same workload."""
     import oracle
@@ -145,6 +172,9 @@ def main() -> int:
     ap.add_argument("--clock-seconds", type=float, default=0.0,
                     help="after timing, repeat the step for this many seconds while sampling the "
                          "shader clock with rocm-smi; reports the median as sclk_mhz")
+    ap.add_argument("--flush-mib", type=int, default=512,
+                    help="MiB written to a scratch buffer before each timed step, outside its events "
+                         "(0: no flush)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (3 times), the "
                          "reference for scaling FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -199,6 +229,10 @@ def main() -> int:
     cur = torch.cuda.current_stream
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
+    ev_step = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    flush_buf = (torch.empty(args.flush_mib << 18, dtype=torch.float32, device=dev)
+                 if args.flush_mib > 0 else None)
 
     gu = None  # training: the gate/up pre-activations the forward keeps for the backward
 
@@ -283,21 +317,40 @@ def main() -> int:
         for _ in range(args.warmup):
             graph.replay()
 
+    # K timed steps, each after a flush and between its own events (median)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if flush_buf is not None:
+            flush_buf.fill_(float(i))
+        ev_step[i][0].record(cur())
+        if graph is not None:
+            graph.replay()
+        else:
+            step(i)
+        ev_step[i][1].record(cur())
+    torch.cuda.synchronize()
+    wall_flushed_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    step_ms = [a.elapsed_time(b) for a, b in ev_step]
+    ms_step = float(np.median(step_ms))
+    if graph is not None:  # the GEMM's events come from an eager pass after the timed replays
+        for i in range(args.steps):
+            if flush_buf is not None:
+                flush_buf.fill_(float(i))
+            step(i)
+        torch.cuda.synchronize()
+    gemm_all = [a.elapsed_time(b) for a, b in ev]
+    gemm_ms = float(np.median(gemm_all))
+    # the same K steps back to back, no flush: wall clock per step
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         if graph is not None:
             graph.replay()
         else:
-            step(i)
+            step()
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_step = elapsed * 1e3 / args.steps
-    if graph is not None:  # the GEMM's events come from an eager pass after the timed replays
-        for i in range(args.steps):
-            step(i)
-        torch.cuda.synchronize()
-    gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    b2b_ms = (time.perf_counter() - t0) * 1e3 / args.steps
 
     # forward: gate/up (4 N d d_ff) + down (2 N d d_ff); backward (the forward kept the gate/up
     # pre-activations): dH (2), dX (4), dW_dn (2), dW_gu (4)
@@ -333,7 +386,9 @@ def main() -> int:
         "traffic": None if train else stored_traffic(w.name),
         "flops_per_launch": flops,
         "algorithmic_bytes_per_launch": gemm_bytes,
-        "avg_ms": round(gemm_ms, 4),
+        "median_ms": round(gemm_ms, 4),
+        "mean_ms": round(float(np.mean(gemm_all)), 4),
+        "timings": len(gemm_all),
     }
     result = {
         "metric": METRIC,
@@ -354,8 +409,18 @@ def main() -> int:
                    "launch": "hip graph" if args.graph else "eager",
                    "step": "forward + backward" if args.train else "forward"},
         "local_pairs_per_s": round(n_loc / (ms_step * 1e-3), 1),
+        "timing": {"per_step": f"median of {args.steps} per-step event times, each step after a "
+                               f"{args.flush_mib} MiB flush write outside its events",
+                   "step_ms_min": round(float(np.min(step_ms)), 4),
+                   "step_ms_max": round(float(np.max(step_ms)), 4),
+                   "wall_ms_per_step_incl_flush": round(wall_flushed_ms, 4),
+                   "back_to_back_ms_per_step": round(b2b_ms, 4)},
         "roofline": roofline,
         "cpu_baseline": None,
+        "seed": w.seed,
+        "inputs_sha256": {"logits": sha256_of(logits), "x": sha256_of(x), "w_gate_up": sha256_of(wgu),
+                          "w_down": sha256_of(wdn)},
+        "versions": versions(torch),
     }
     # per entry point, in a separate untimed pass: events between the calls
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]

@@ -10,9 +10,11 @@
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is a DEVICE pointer to a dense row-major array that
- *     the caller allocates and owns. The library allocates nothing and keeps no
- *     global mutable state; calls on different streams may run concurrently
- *     when they write disjoint buffers.
+ *     the caller allocates and owns. The library allocates nothing. Its only
+ *     process-wide state is a per-device cache of the compute-unit count (read
+ *     once per device with hipDeviceGetAttribute, filled atomically, never
+ *     changed afterwards), which sizes the persistent GEMM grids. Calls on
+ *     different streams may run concurrently when they write disjoint buffers.
  *   - Every call validates its arguments on the host, enqueues its kernels on
  *     `stream` and returns without synchronising. Invalid arguments return
  *     MOE_EINVAL (or MOE_EUNSUPPORTED for a valid but unsupported shape) before
@@ -111,11 +113,24 @@ size_t moe_dispatch_workspace_bytes(const moe_shape* s);
  *            [e_begin] + r] / k]; rows past N_loc are left unwritten.
  *   workspace moe_dispatch_workspace_bytes(s) bytes of device memory (may be
  *            NULL when that is 0); contents on entry do not matter.
- * T = 0 still writes counts and offsets (all zero). */
+ * T = 0 still writes counts and offsets (all zero). MOE_EINVAL if workspace is
+ * NULL while moe_dispatch_workspace_bytes(s) > 0. */
 moe_status moe_dispatch(const moe_shape* s, moe_dtype dt, const void* x,
                         const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
                         int32_t* perm, int32_t* pair_pos, void* x_perm,
                         void* workspace, hipStream_t stream);
+
+/* Debug builds. The library compiled with MOE_DEBUG defined (libmoe_debug.so,
+ * built beside libmoe.so) also checks on the device the expert ids that
+ * moe_dispatch and moe_dispatch_indices receive, where the release build drops
+ * an id outside [0, E) without a trace ("Paralelismo de especialistas",
+ * "Sobrescrevendo os planos": invalid input is refused rather than sharded).
+ * Each call then writes an int32 error word into its workspace, at byte offset
+ * moe_dispatch_debug_word_offset(): the number of ids outside [0, E) in
+ * topk_idx, 0 when every id is valid (T = 0 writes 0). It is rewritten by every
+ * call; read it once the stream has passed the call. The outputs are those of
+ * the release build. Returns SIZE_MAX in release builds (no error word). */
+size_t moe_dispatch_debug_word_offset(void);
 
 /* moe_dispatch without the row gather: counts, offsets, perm and pair_pos as
  * moe_dispatch writes them, and no x_perm. For the fused path, in which

@@ -146,23 +146,35 @@ def expert_ffn(rows: np.ndarray, w_gate_up: np.ndarray, w_down: np.ndarray) -> n
 
 
 def grouped_experts(x_perm: np.ndarray, offsets: np.ndarray, e_lo: int, e_hi: int,
-                    w_gate_up, w_down) -> np.ndarray:
+                    w_gate_up, w_down, return_hidden: bool = False):
     """experts_forward of [EP] "Adicionando uma implementação": run each local
     expert on its contiguous segment of x_perm. w_gate_up / w_down are indexed
     by local expert (sharded along the expert dimension, [EP] GroupedGemmParallel)
     and may be arrays or callables e -> matrix. Experts with no rows are skipped.
+
+    Each segment is expert_ffn taken in its two steps, H = swiglu_hidden(rows)
+    then Y = H @ W_dn. Returns Y [N_loc, d], or (H [N_loc, d_ff], Y) with
+    return_hidden.
     """
     x_perm = np.asarray(x_perm, dtype=np.float64)
     d = x_perm.shape[1] if x_perm.ndim == 2 else 0
     base = offsets[e_lo]
     y = np.zeros((x_perm.shape[0], d), dtype=np.float64)
+    h = None
     for e in range(e_lo, e_hi):
         r0, r1 = offsets[e] - base, offsets[e + 1] - base
         if r1 == r0:
             continue
         wgu = w_gate_up(e - e_lo) if callable(w_gate_up) else w_gate_up[e - e_lo]
         wdn = w_down(e - e_lo) if callable(w_down) else w_down[e - e_lo]
-        y[r0:r1] = expert_ffn(x_perm[r0:r1], wgu, wdn)
+        h_e = swiglu_hidden(x_perm[r0:r1], wgu)
+        if return_hidden:
+            if h is None:
+                h = np.zeros((x_perm.shape[0], h_e.shape[1]), dtype=np.float64)
+            h[r0:r1] = h_e
+        y[r0:r1] = h_e @ np.asarray(wdn, dtype=np.float64)
+    if return_hidden:
+        return (h if h is not None else np.zeros((x_perm.shape[0], 0))), y
     return y
 
 
@@ -188,17 +200,17 @@ def combine(y: np.ndarray, pair_pos: np.ndarray, w: np.ndarray, T: int, k: int, 
 def moe_layer(x, logits, k: int, e_lo: int, e_hi: int, w_gate_up, w_down):
     """The whole forward of one rank: route -> dispatch -> experts -> combine.
 
-    Returns a dict with every intermediate the GPU path exposes.
+    Returns a dict with every intermediate the GPU path exposes (H included).
     """
     x = np.asarray(x, dtype=np.float64)
     T, d = x.shape
     E = logits.shape[1]
     idx, w = route_topk(logits, k)
     counts, offsets, perm, pair_pos, x_perm = dispatch(idx, E, e_lo, e_hi, x)
-    y = grouped_experts(x_perm, offsets, e_lo, e_hi, w_gate_up, w_down)
+    h, y = grouped_experts(x_perm, offsets, e_lo, e_hi, w_gate_up, w_down, return_hidden=True)
     out = combine(y, pair_pos, w, T, k, d)
     return dict(idx=idx, w=w, counts=counts, offsets=offsets, perm=perm,
-                pair_pos=pair_pos, x_perm=x_perm, y=y, out=out)
+                pair_pos=pair_pos, x_perm=x_perm, h=h, y=y, out=out)
 
 
 def brute_force_dense(x, idx, w, e_lo: int, e_hi: int, w_gate_up, w_down) -> np.ndarray:

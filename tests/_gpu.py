@@ -40,6 +40,17 @@ def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     return float(err / scale)
 
 
+def row_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """The worst row of max |got - ref| / max |ref| taken row by row; a row whose
+    reference is all zero counts its largest |got - ref| (0 when both are zero)."""
+    if ref.size == 0:
+        return 0.0
+    scale = np.abs(ref).max(axis=1)
+    err = np.abs(got - ref).max(axis=1)
+    zero = scale == 0
+    return float(np.where(zero, err, err / np.where(zero, 1.0, scale)).max())
+
+
 # max |err| / max |ref| bound on floating outputs: bf16 activations and weights
 # with fp32 accumulation, fp32 throughout for the fp32 path.
 TOL = {"bf16": 2e-2, "f32": 1e-5}

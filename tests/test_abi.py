@@ -195,3 +195,28 @@ def test_backward_entry_points_validate_on_the_host():
     assert lib.moe_grouped_gemm_backward_workspace_bytes(ctypes.byref(s), moe.MOE_BF16) == \
         n_max * 64 * 2 + 2 * n_max * 128 * 2
     assert lib.moe_grouped_gemm_backward_workspace_bytes(ctypes.byref(s), moe.MOE_F32) == 0
+
+
+# ----------------------------------------------------------------------------- debug build
+
+debug_built = pytest.mark.skipif(not os.path.exists(moe.debug_lib_path), reason="libmoe_debug.so not built")
+
+
+@debug_built
+def test_debug_library_exports_every_declared_symbol_and_has_the_error_word():
+    release = moe.lib()
+    assert release.moe_dispatch_debug_word_offset() == moe._SIZE_MAX
+    moe.set_debug(True)
+    try:
+        lib = moe.lib()
+        for name in moe.declared_symbols():
+            assert hasattr(lib, name), name
+        assert lib.moe_dispatch_debug_word_offset() == 0
+        # the word needs workspace even when there are no pairs, and a call without it is refused
+        assert moe.dispatch_workspace_bytes(0, 2, 8) >= 4
+        s = _shape(T=0)
+        assert lib.moe_dispatch_indices(ctypes.byref(s), NULL, FAKE, FAKE, NULL, NULL, NULL, NULL) == moe.MOE_EINVAL
+        assert moe.dispatch_workspace_bytes(100, 2, 8) > 4
+    finally:
+        moe.set_debug(False)
+    assert moe.dispatch_workspace_bytes(0, 2, 8) == 0

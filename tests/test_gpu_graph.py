@@ -5,13 +5,15 @@ masking variant that keeps shapes static).
 Every step of the layer takes its sizes from the host-side shape and its row
 counts from device memory, allocates nothing and never synchronises, so the
 four calls capture as they are. Each replay runs on new inputs copied into the
-captured buffers, with eager work and synchronisations between replays, and
-must equal the eager layer on the same inputs bit for bit.
+captured buffers, with eager work and synchronisations between replays. It must
+equal the eager layer on the same inputs bit for bit, and the oracle on those
+inputs (ids exactly, floating results within max|err|/max|ref| <= 2e-2).
 """
 import numpy as np
 import pytest
 
 import moe_inputs as mi
+import oracle
 from tests import _gpu as g
 
 pytestmark = pytest.mark.gpu
@@ -92,6 +94,13 @@ def test_layer_graph_replays_match_eager(fused):
         assert torch.equal(got_idx, eager["idx"]), seed
         assert torch.equal(got, eager["out"]), seed
         assert torch.count_nonzero(got).item() > 0
+        # and the oracle on the replay's inputs
+        ref = oracle.moe_layer(mi.to_f64(x, "bf16"), lg, w.k, w.e_begin, w.e_end, mi.to_f64(wgu, "bf16"),
+                               mi.to_f64(wdn, "bf16"))
+        np.testing.assert_array_equal(got_idx.cpu().numpy(), ref["idx"])
+        err = g.rel_err(g.to_f64(got), ref["out"])
+        print(f"  replay {seed}: out max|err|/max|ref| = {err:.3e}", flush=True)
+        assert err <= g.TOL["bf16"], (seed, err)
 
 
 def test_training_step_graph_replays_match_eager():
@@ -170,3 +179,11 @@ def test_training_step_graph_replays_match_eager():
                 a, e = a.view(torch.int16), e.view(torch.int16)
             assert torch.equal(a, e), (seed, key)
         assert torch.count_nonzero(got["d_w_gate_up"]).item() > 0
+        # and the oracle's forward and gradient on the replay's inputs
+        ref = oracle.moe_layer_backward(mi.to_f64(x, "bf16"), lg, w.k, w.e_begin, w.e_end,
+                                        list(mi.to_f64(wgu, "bf16")), list(mi.to_f64(wdn, "bf16")),
+                                        mi.to_f64(do, "bf16"))
+        errs = {key: g.rel_err(t.float().cpu().numpy().astype(np.float64), ref[key]) for key, t in got.items()}
+        print(f"  replay {seed}: " + ", ".join(f"{k_} {v:.2e}" for k_, v in errs.items()), flush=True)
+        for key, err in errs.items():
+            assert err <= g.TOL["bf16"], (seed, key, err)

@@ -184,20 +184,28 @@ def test_layer_zero_tokens():
 
 
 def test_rank_sum_on_one_gpu():
-    """Masked partial outputs of every rank's share add up to the full layer."""
+    """Masked partial outputs of every rank's share: each equals the oracle's
+    partial output of that rank, and they add up to the oracle's full layer."""
     base = mi.Workload("rank_sum", 512, 192, 128, 16, 4, 0, 16, "bf16", 20)
-    logits = g.to_dev(mi.router_logits(base), "f32")
-    x = g.to_dev(mi.hidden_states(base), "bf16")
+    logits_np, x_np = mi.router_logits(base), mi.hidden_states(base)
+    logits = g.to_dev(logits_np, "f32")
+    x = g.to_dev(x_np, "bf16")
     wgu_np, wdn_np = mi.expert_weights(base)
     wgu, wdn = g.to_dev(wgu_np, "bf16"), g.to_dev(wdn_np, "bf16")
-    full = moe.layer(x, logits, wgu, wdn, base.k, 0, 16)["out"].float()
+    x64, wgu64, wdn64 = mi.to_f64(x_np, "bf16"), mi.to_f64(wgu_np, "bf16"), mi.to_f64(wdn_np, "bf16")
+    full_ref = oracle.moe_layer(x64, logits_np, base.k, 0, 16, wgu64, wdn64)["out"]
+    full = g.to_f64(moe.layer(x, logits, wgu, wdn, base.k, 0, 16)["out"])
+    assert g.rel_err(full, full_ref) <= 2e-2
     for ep in (2, 4, 8):
-        acc = torch.zeros_like(full)
+        acc = np.zeros_like(full)
         for r in range(ep):
             lo, hi = moe.expert_range(16, ep, r)
-            acc += moe.layer(x, logits, wgu[lo:hi].contiguous(), wdn[lo:hi].contiguous(), base.k, lo, hi)["out"].float()
-        torch.cuda.synchronize()
-        err = g.rel_err(acc.cpu().numpy().astype(np.float64), full.cpu().numpy().astype(np.float64))
+            part = g.to_f64(moe.layer(x, logits, wgu[lo:hi].contiguous(), wdn[lo:hi].contiguous(), base.k, lo,
+                                      hi)["out"])
+            part_ref = oracle.moe_layer(x64, logits_np, base.k, lo, hi, wgu64[lo:hi], wdn64[lo:hi])["out"]
+            assert g.rel_err(part, part_ref) <= 2e-2, (ep, r)
+            acc += part
+        err = g.rel_err(acc, full_ref)
         assert err <= 2e-2, (ep, err)
 
 
@@ -297,12 +305,18 @@ def test_layer_split_after_full_rounds():
     _fused_matches_staged(w, mi.router_logits(w), res, ref)
 
 
-@pytest.mark.parametrize("w", [SMALL[3], SMALL[4], mi.Workload("regs_heights", 600, 256, 192, 8, 2, 0, 8, "bf16", 24)],
-                         ids=["skew_small", "decode_small", "heights"])
-def test_layer_register_staged_kernel(w, monkeypatch):
-    """The register-staged GEMM (used when d or d_ff is not a multiple of 32) on
-    shapes the pipelined kernel would otherwise take."""
-    monkeypatch.setenv("MOE_GEMM_KERNEL", "regs")
+REGS = [mi.Workload("regs_skew", 1000, 328, 136, 64, 8, 0, 16, "bf16", 13, 1.5),      # skewed, empty experts
+        mi.Workload("regs_decode", 5, 264, 200, 128, 4, 0, 128, "bf16", 14),         # mostly empty experts
+        mi.Workload("regs_heights", 600, 264, 200, 8, 2, 0, 8, "bf16", 24),
+        mi.Workload("regs_d_only", 700, 328, 192, 8, 2, 0, 8, "bf16", 33),            # d_ff a multiple of 32
+        mi.Workload("regs_dff_only", 700, 256, 200, 8, 2, 0, 8, "bf16", 34)]          # d a multiple of 32
+
+
+@pytest.mark.parametrize("w", REGS, ids=[w.name for w in REGS])
+def test_layer_register_staged_kernel(w):
+    """The register-staged GEMM, which takes every shape whose d or d_ff is a
+    multiple of 8 but not of 32, on skewed, decode-shaped and multi-tile inputs."""
+    assert w.d % 32 or w.d_ff % 32
     _layer_case(w)
 
 
@@ -445,3 +459,40 @@ def test_layers_on_two_streams_from_two_threads():
     for i in range(2):
         for out in got[i]:
             assert torch.equal(out.view(torch.int16), alone[i].view(torch.int16)), i
+
+
+# ----------------------------------------------------------------------------- debug build
+
+@pytest.mark.parametrize("T,E,k", [(300, 8, 2), (3000, 64, 4), (0, 16, 2)], ids=["one_workgroup", "chunked", "empty"])
+def test_debug_build_refuses_out_of_range_ids(T, E, k):
+    """libmoe_debug.so counts the ids outside [0, E) on the device and the binding
+    refuses them; valid ids give the release build's results bit for bit."""
+    rng = np.random.default_rng(T + E)
+    d = 64
+    x = g.to_dev(mi.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32)), "bf16")
+    good = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    release = moe.dispatch(x, torch.from_numpy(good).cuda(), E, 0, E // 2)
+    torch.cuda.synchronize()
+    moe.set_debug(True)
+    try:
+        dbg = moe.dispatch(x, torch.from_numpy(good).cuda(), E, 0, E // 2)
+        torch.cuda.synchronize()
+        for key in ("counts", "offsets", "perm", "pair_pos"):
+            assert torch.equal(getattr(dbg, key), getattr(release, key)), key
+        n = dbg.offsets[E // 2].item()
+        assert torch.equal(dbg.x_perm[:n].view(torch.int16), release.x_perm[:n].view(torch.int16))
+        if T == 0:
+            return
+        bad = good.copy()
+        flat = bad.reshape(-1)
+        where = rng.choice(flat.size, size=7, replace=False)
+        flat[where[:4]] = -1 - where[:4].astype(np.int32)
+        flat[where[4:]] = E + where[4:].astype(np.int32)
+        with pytest.raises(ValueError, match=r"holds 7 expert id\(s\) outside"):
+            moe.dispatch(x, torch.from_numpy(bad).cuda(), E, 0, E // 2)
+        with pytest.raises(ValueError, match=r"holds 7 expert id\(s\) outside"):
+            moe.dispatch(x, torch.from_numpy(bad).cuda(), E, 0, E // 2, gather=False)
+        # the word is rewritten by every call: valid ids pass again on the same buffers
+        moe.dispatch(x, torch.from_numpy(good).cuda(), E, 0, E // 2, out=dbg)
+    finally:
+        moe.set_debug(False)

@@ -225,6 +225,39 @@ def test_worked_example():
     check_worked_example(oracle.route_topk, oracle.dispatch, oracle.moe_layer)
 
 
+def check_layer_hidden(moe_layer):
+    """H and Y of the worked example: gate_up = [I | 2I] gives H = silu(x) * 2x =
+    2 x^2 sigmoid(x) on the gathered rows (tokens 1 and 2), and a down
+    projection that swaps the two columns gives Y = H with its columns swapped."""
+    g, logits = _worked()
+    x = np.array(g["x"])
+    wgu, _ = _worked_weights()
+    swap = np.array([[0.0, 1.0], [1.0, 0.0]])
+    res = moe_layer(x, logits, g["k"], g["e_lo"], g["e_hi"], wgu, np.stack([swap, swap]))
+    rows = x[g["x_perm_tokens"]]
+    np.testing.assert_allclose(res["h"], 2.0 * rows * rows * expit(rows), rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(res["y"], res["h"][:, ::-1], rtol=1e-14, atol=1e-15)
+
+
+def test_layer_hidden_closed_form():
+    check_layer_hidden(oracle.moe_layer)
+
+
+def test_planted_hidden_mistakes_are_caught():
+    def layer_gate_only(x, logits, k, e_lo, e_hi, wgu, wdn):
+        res = om.moe_layer(x, logits, k, e_lo, e_hi, wgu, wdn)
+        res["h"] = om.silu(res["x_perm"])  # silu(gate) without the up projection
+        return res
+
+    def layer_unprojected(x, logits, k, e_lo, e_hi, wgu, wdn):
+        res = om.moe_layer(x, logits, k, e_lo, e_hi, wgu, wdn)
+        res["y"] = res["h"]  # down projection dropped
+        return res
+
+    _fails(check_layer_hidden, layer_gate_only)
+    _fails(check_layer_hidden, layer_unprojected)
+
+
 def test_topk_properties():
     check_topk_properties(oracle.route_topk)
 

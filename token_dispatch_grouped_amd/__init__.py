@@ -5,6 +5,16 @@ runs in the library's HIP kernels; PyTorch only provides device memory and the
 current stream. There is no fallback: if the library is missing, importing the
 binding works only for introspection (`lib_path`, `declared_symbols`) and every
 compute call raises.
+
+Every wrapper checks the dtype and shape of each tensor it is given (inputs and
+caller-provided outputs alike) against the sizes of the call before anything
+reaches the library: a wrong dtype raises TypeError, a wrong shape ValueError.
+
+Debug mode (`set_debug(True)`, or MOE_DEBUG=1 in the environment at import)
+loads libmoe_debug.so instead, whose dispatch also counts the expert ids outside
+[0, E) on the device; `dispatch` then waits for its stream and raises ValueError
+when there are any. That wait makes the dispatch synchronous, so debug mode is
+for finding bad input, not for graph capture or timing.
 """
 from __future__ import annotations
 
@@ -16,7 +26,9 @@ from dataclasses import dataclass
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_PKG)
 lib_path = os.path.join(_PKG, "libmoe.so")
+debug_lib_path = os.path.join(_PKG, "libmoe_debug.so")
 header_path = os.path.join(_ROOT, "include", "moe.h")
+_SIZE_MAX = ctypes.c_size_t(-1).value
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP = 0, 1, 2, 3
 MOE_F32, MOE_BF16 = 0, 1
@@ -40,23 +52,35 @@ class moe_shape(ctypes.Structure):
     ]
 
 
-_lib = None
+_libs: dict = {}
+_debug = os.environ.get("MOE_DEBUG", "") not in ("", "0")
+
+
+def set_debug(enabled: bool) -> None:
+    """Use libmoe_debug.so (True) or libmoe.so (False) for the calls that follow."""
+    global _debug
+    _debug = bool(enabled)
+
+
+def debug_enabled() -> bool:
+    return _debug
 
 
 def _load():
-    global _lib
-    if _lib is None:
-        if not os.path.exists(lib_path):
+    path = debug_lib_path if _debug else lib_path
+    if path not in _libs:
+        if not os.path.exists(path):
             raise ImportError(
-                f"{lib_path} is missing: build it with token_dispatch_grouped_amd.build.build() "
+                f"{path} is missing: build it with token_dispatch_grouped_amd.build.build() "
                 "(there is no fallback path)")
-        lib = ctypes.CDLL(lib_path)
+        lib = ctypes.CDLL(path)
         P, S, I32, I64, SZ = ctypes.c_void_p, ctypes.POINTER(moe_shape), ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         sigs = {
             "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "moe_expert_range": (ctypes.c_int, [I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
             "moe_route_topk": (ctypes.c_int, [S, P, P, P, P]),
             "moe_dispatch_workspace_bytes": (SZ, [S]),
+            "moe_dispatch_debug_word_offset": (SZ, []),
             "moe_dispatch": (ctypes.c_int, [S, ctypes.c_int, P, P, P, P, P, P, P, P, P]),
             "moe_dispatch_indices": (ctypes.c_int, [S, P, P, P, P, P, P, P]),
             "moe_grouped_gemm_gather": (ctypes.c_int, [S, ctypes.c_int, P, P, P, P, P, P, P, P, P]),
@@ -76,8 +100,8 @@ def _load():
             fn = getattr(lib, name)
             fn.restype = res
             fn.argtypes = args
-        _lib = lib
-    return _lib
+        _libs[path] = lib
+    return _libs[path]
 
 
 def lib():
@@ -141,6 +165,57 @@ def _dev(*ts):
             raise ValueError("every tensor must be contiguous (row-major)")
 
 
+def _want(t, name: str, dtype=None, shape=None, min_rows=None):
+    """Check one tensor argument: its dtype (TypeError) and its shape (ValueError).
+    `shape` is the exact shape; with `min_rows`, shape[0] may be any count of at
+    least min_rows (a buffer sized for more rows than this call's N_max)."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if dtype is not None:
+        allowed = dtype if isinstance(dtype, tuple) else (dtype,)
+        if t.dtype not in allowed:
+            want = " or ".join(str(a) for a in allowed)
+            raise TypeError(f"{name} must be {want}, got {t.dtype}")
+    if shape is not None:
+        got = tuple(t.shape)
+        if min_rows is not None:
+            ok = len(got) == len(shape) and got[1:] == tuple(shape[1:]) and got[0] >= min_rows
+            if not ok:
+                raise ValueError(f"{name} must have shape [>= {min_rows}, {', '.join(map(str, shape[1:]))}], "
+                                 f"got {list(got)}")
+        elif got != tuple(shape):
+            raise ValueError(f"{name} must have shape {list(shape)}, got {list(got)}")
+
+
+def _act_dtypes():
+    torch = _torch()
+    return (torch.bfloat16, torch.float32)
+
+
+def _n_max(T: int, k: int, e_begin: int, e_end: int) -> int:
+    return T * min(k, e_end - e_begin)
+
+
+def _expert_weights(w_gate_up, w_down, dtype, d: int, e_begin: int, e_end: int) -> int:
+    """Checks the local experts' weights against the activations; returns d_ff."""
+    _want(w_down, "w_down", dtype)
+    if w_down.dim() != 3:
+        raise ValueError(f"w_down must be [E_loc, d_ff, d], got {list(w_down.shape)}")
+    e_loc, d_ff = int(w_down.shape[0]), int(w_down.shape[1])
+    if e_loc != e_end - e_begin:
+        raise ValueError(f"expert weights must hold exactly the {e_end - e_begin} local experts, got {e_loc}")
+    _want(w_down, "w_down", dtype, (e_loc, d_ff, d))
+    _want(w_gate_up, "w_gate_up", dtype, (e_loc, d, 2 * d_ff))
+    return d_ff
+
+
+def _range(E: int, k: int, e_begin: int, e_end: int) -> None:
+    if not 1 <= k <= E:
+        raise ValueError(f"need 1 <= k <= E, got k={k}, E={E}")
+    if not 0 <= e_begin < e_end <= E:
+        raise ValueError(f"local experts [{e_begin}, {e_end}) must be a non-empty range inside [0, {E})")
+
+
 def shape(T, d, d_ff, E, k, e_begin, e_end) -> moe_shape:
     return moe_shape(int(T), int(d), int(d_ff), int(E), int(k), int(e_begin), int(e_end))
 
@@ -156,15 +231,21 @@ def expert_range(E: int, ep: int, rank: int) -> tuple[int, int]:
 def route_topk(logits, k: int, topk_idx=None, topk_w=None, stream=None):
     """logits [T, E] fp32 -> (topk_idx [T, k] int32, topk_w [T, k] fp32)."""
     torch = _torch()
-    _dev(logits)
-    if logits.dtype != torch.float32 or logits.dim() != 2:
-        raise TypeError("logits must be a [T, E] float32 tensor")
-    T, E = logits.shape
+    _want(logits, "logits", torch.float32)
+    if logits.dim() != 2:
+        raise ValueError(f"logits must be [T, E], got {list(logits.shape)}")
+    T, E = (int(v) for v in logits.shape)
+    if not 1 <= k <= E:
+        raise ValueError(f"need 1 <= k <= E, got k={k}, E={E}")
+    if topk_idx is not None:
+        _want(topk_idx, "topk_idx", torch.int32, (T, k))
+    if topk_w is not None:
+        _want(topk_w, "topk_w", torch.float32, (T, k))
+    _dev(logits, topk_idx, topk_w)
     if topk_idx is None:
         topk_idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
     if topk_w is None:
         topk_w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
-    _dev(topk_idx, topk_w)
     s = shape(T, 8, 8, E, k, 0, E)
     _check(_load().moe_route_topk(ctypes.byref(s), _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _stream(stream)),
            "moe_route_topk")
@@ -181,14 +262,18 @@ class Dispatch:
     workspace: object
 
 
+def dispatch_workspace_bytes(T: int, k: int, E: int) -> int:
+    s = shape(T, 8, 8, E, k, 0, E)
+    return int(_load().moe_dispatch_workspace_bytes(ctypes.byref(s)))
+
+
 def dispatch_alloc(x, k: int, E: int, e_begin: int, e_end: int, gather: bool = True) -> Dispatch:
     """Allocate every dispatch output (sized on the host, no device read); without
     `gather` there is no x_perm (the fused path reads rows straight from x)."""
     torch = _torch()
     T, d = x.shape
-    n_max = T * min(k, e_end - e_begin)
-    s = shape(T, d, 8, E, k, e_begin, e_end)
-    ws_bytes = _load().moe_dispatch_workspace_bytes(ctypes.byref(s))
+    n_max = _n_max(T, k, e_begin, e_end)
+    ws_bytes = dispatch_workspace_bytes(T, k, E)
     dev = x.device
     return Dispatch(
         counts=torch.empty(E, dtype=torch.int32, device=dev),
@@ -200,19 +285,57 @@ def dispatch_alloc(x, k: int, E: int, e_begin: int, e_end: int, gather: bool = T
     )
 
 
+def _check_dispatch(out: Dispatch, x, T: int, k: int, E: int, n_max: int, gather: bool) -> None:
+    torch = _torch()
+    _want(out.counts, "counts", torch.int32, (E,))
+    _want(out.offsets, "offsets", torch.int32, (E + 1,))
+    _want(out.perm, "perm", torch.int32, (T * k,))
+    _want(out.pair_pos, "pair_pos", torch.int32, (T * k,))
+    if gather:
+        if out.x_perm is None:
+            raise ValueError("this Dispatch has no x_perm; allocate it with gather=True")
+        _want(out.x_perm, "x_perm", x.dtype, (n_max, x.shape[1]), min_rows=n_max)
+    _want(out.workspace, "workspace", torch.uint8)
+    need = dispatch_workspace_bytes(T, k, E)
+    if out.workspace.numel() < need:
+        raise ValueError(f"workspace must hold at least {need} bytes, got {out.workspace.numel()}")
+
+
+def _debug_word(out: Dispatch, E: int, stream) -> None:
+    """Debug mode: wait for the dispatch, then refuse ids outside [0, E)."""
+    torch = _torch()
+    off = int(_load().moe_dispatch_debug_word_offset())
+    if off == _SIZE_MAX:
+        return
+    (stream if stream is not None else torch.cuda.current_stream()).synchronize()
+    bad = int(out.workspace[off:off + 4].view(torch.int32).item())
+    if bad:
+        raise ValueError(f"moe_dispatch: topk_idx holds {bad} expert id(s) outside [0, {E})")
+
+
 def dispatch(x, topk_idx, E: int, e_begin: int, e_end: int, out: Dispatch | None = None, stream=None,
              gather: bool = True) -> Dispatch:
     """Histogram, offsets, stable permutation and (with `gather`) the local-row
     gather into x_perm; without it, moe_dispatch_indices (no x_perm)."""
+    torch = _torch()
+    _want(x, "x", _act_dtypes())
+    if x.dim() != 2:
+        raise ValueError(f"x must be [T, d], got {list(x.shape)}")
+    T, d = (int(v) for v in x.shape)
+    _want(topk_idx, "topk_idx", torch.int32)
+    if topk_idx.dim() != 2 or topk_idx.shape[0] != T:
+        raise ValueError(f"topk_idx must be [T={T}, k], got {list(topk_idx.shape)}")
+    k = int(topk_idx.shape[1])
+    _range(E, k, e_begin, e_end)
+    n_max = _n_max(T, k, e_begin, e_end)
+    if out is not None:
+        _check_dispatch(out, x, T, k, E, n_max, gather)
     _dev(x, topk_idx)
-    T, d = x.shape
-    k = topk_idx.shape[1] if topk_idx.dim() == 2 else 1
     if out is None:
         out = dispatch_alloc(x, k, E, e_begin, e_end, gather=gather)
+    _dev(out.counts, out.offsets, out.perm, out.pair_pos, out.x_perm if gather else None, out.workspace)
     s = shape(T, d, 8, E, k, e_begin, e_end)
     if gather:
-        if out.x_perm is None:
-            raise ValueError("this Dispatch has no x_perm; allocate it with gather=True")
         _check(_load().moe_dispatch(ctypes.byref(s), _dtype_code(x), _ptr(x), _ptr(topk_idx), _ptr(out.counts),
                                     _ptr(out.offsets), _ptr(out.perm), _ptr(out.pair_pos), _ptr(out.x_perm),
                                     _ptr(out.workspace), _stream(stream)), "moe_dispatch")
@@ -220,25 +343,39 @@ def dispatch(x, topk_idx, E: int, e_begin: int, e_end: int, out: Dispatch | None
         _check(_load().moe_dispatch_indices(ctypes.byref(s), _ptr(topk_idx), _ptr(out.counts), _ptr(out.offsets),
                                             _ptr(out.perm), _ptr(out.pair_pos), _ptr(out.workspace),
                                             _stream(stream)), "moe_dispatch_indices")
+    if _debug:
+        _debug_word(out, E, stream)
     return out
+
+
+def _gemm_outputs(h, y, n_max: int, d: int, d_ff: int, dtype, device):
+    torch = _torch()
+    if h is None:
+        h = torch.empty((n_max, d_ff), dtype=dtype, device=device)
+    else:
+        _want(h, "h", dtype, (n_max, d_ff), min_rows=n_max)
+    if y is None:
+        y = torch.empty((n_max, d), dtype=dtype, device=device)
+    else:
+        _want(y, "y", dtype, (n_max, d), min_rows=n_max)
+    return h, y
 
 
 def grouped_gemm(x_perm, offsets, w_gate_up, w_down, T: int, k: int, E: int, e_begin: int, e_end: int,
                  h=None, y=None, stream=None):
     """Local experts' SwiGLU FFN: returns (h [N_max, d_ff], y [N_max, d])."""
     torch = _torch()
-    _dev(x_perm, offsets, w_gate_up, w_down)
-    n_max, d = x_perm.shape
-    e_loc, d_ff, _ = w_down.shape
-    if w_gate_up.shape != (e_loc, d, 2 * d_ff) or w_down.shape != (e_loc, d_ff, d):
-        raise ValueError("w_gate_up must be [E_loc, d, 2*d_ff] and w_down [E_loc, d_ff, d]")
-    if e_loc != e_end - e_begin:
-        raise ValueError("expert weights must hold exactly the local experts")
-    if h is None:
-        h = torch.empty((n_max, d_ff), dtype=x_perm.dtype, device=x_perm.device)
-    if y is None:
-        y = torch.empty((n_max, d), dtype=x_perm.dtype, device=x_perm.device)
-    _dev(h, y)
+    _range(E, k, e_begin, e_end)
+    n_max = _n_max(T, k, e_begin, e_end)
+    _want(x_perm, "x_perm", _act_dtypes())
+    if x_perm.dim() != 2:
+        raise ValueError(f"x_perm must be [N_max, d], got {list(x_perm.shape)}")
+    d = int(x_perm.shape[1])
+    _want(x_perm, "x_perm", x_perm.dtype, (n_max, d), min_rows=n_max)
+    _want(offsets, "offsets", torch.int32, (E + 1,))
+    d_ff = _expert_weights(w_gate_up, w_down, x_perm.dtype, d, e_begin, e_end)
+    h, y = _gemm_outputs(h, y, n_max, d, d_ff, x_perm.dtype, x_perm.device)
+    _dev(x_perm, offsets, w_gate_up, w_down, h, y)
     s = shape(T, d, d_ff, E, k, e_begin, e_end)
     dt = _dtype_code(x_perm)
     ws_bytes = _load().moe_grouped_gemm_workspace_bytes(ctypes.byref(s), dt)
@@ -256,19 +393,19 @@ def grouped_gemm_gather(x, perm, offsets, w_gate_up, w_down, k: int, E: int, e_b
     dispatch + grouped_gemm. With gu (a [N_max, 2*d_ff] tensor) the gate/up
     pre-activations are kept there as well (moe_grouped_gemm_gather_save)."""
     torch = _torch()
-    _dev(x, perm, offsets, w_gate_up, w_down)
-    T, d = x.shape
-    e_loc, d_ff, _ = w_down.shape
-    if w_gate_up.shape != (e_loc, d, 2 * d_ff) or w_down.shape != (e_loc, d_ff, d):
-        raise ValueError("w_gate_up must be [E_loc, d, 2*d_ff] and w_down [E_loc, d_ff, d]")
-    if e_loc != e_end - e_begin:
-        raise ValueError("expert weights must hold exactly the local experts")
-    n_max = T * min(k, e_loc)
-    if h is None:
-        h = torch.empty((n_max, d_ff), dtype=x.dtype, device=x.device)
-    if y is None:
-        y = torch.empty((n_max, d), dtype=x.dtype, device=x.device)
-    _dev(h, y)
+    _range(E, k, e_begin, e_end)
+    _want(x, "x", _act_dtypes())
+    if x.dim() != 2:
+        raise ValueError(f"x must be [T, d], got {list(x.shape)}")
+    T, d = (int(v) for v in x.shape)
+    n_max = _n_max(T, k, e_begin, e_end)
+    _want(perm, "perm", torch.int32, (T * k,))
+    _want(offsets, "offsets", torch.int32, (E + 1,))
+    d_ff = _expert_weights(w_gate_up, w_down, x.dtype, d, e_begin, e_end)
+    h, y = _gemm_outputs(h, y, n_max, d, d_ff, x.dtype, x.device)
+    if gu is not None:
+        _want(gu, "gu", x.dtype, (n_max, 2 * d_ff), min_rows=n_max)
+    _dev(x, perm, offsets, w_gate_up, w_down, h, y, gu)
     s = shape(T, d, d_ff, E, k, e_begin, e_end)
     dt = _dtype_code(x)
     ws_bytes = _load().moe_grouped_gemm_workspace_bytes(ctypes.byref(s), dt)
@@ -278,9 +415,6 @@ def grouped_gemm_gather(x, perm, offsets, w_gate_up, w_down, k: int, E: int, e_b
                                                _ptr(w_gate_up), _ptr(w_down), _ptr(h), _ptr(y), _ptr(ws),
                                                _stream(stream)), "moe_grouped_gemm_gather")
     else:
-        _dev(gu)
-        if tuple(gu.shape) != (n_max, 2 * d_ff) or gu.dtype != x.dtype:
-            raise ValueError("gu must be [N_max, 2*d_ff] in the activations' dtype")
         _check(_load().moe_grouped_gemm_gather_save(ctypes.byref(s), dt, _ptr(x), _ptr(perm), _ptr(offsets),
                                                     _ptr(w_gate_up), _ptr(w_down), _ptr(h), _ptr(y), _ptr(gu),
                                                     _ptr(ws), _stream(stream)), "moe_grouped_gemm_gather_save")
@@ -290,11 +424,20 @@ def grouped_gemm_gather(x, perm, offsets, w_gate_up, w_down, k: int, E: int, e_b
 def combine(y, pair_pos, topk_w, T: int, k: int, E: int, e_begin: int, e_end: int, out=None, stream=None):
     """out[t] = sum_j topk_w[t, j] * y[pair_pos[t*k + j]] over local pairs; [T, d]."""
     torch = _torch()
-    _dev(y, pair_pos, topk_w)
-    d = y.shape[1]
+    _range(E, k, e_begin, e_end)
+    n_max = _n_max(T, k, e_begin, e_end)
+    _want(y, "y", _act_dtypes())
+    if y.dim() != 2:
+        raise ValueError(f"y must be [N_max, d], got {list(y.shape)}")
+    d = int(y.shape[1])
+    _want(y, "y", y.dtype, (n_max, d), min_rows=n_max)
+    _want(pair_pos, "pair_pos", torch.int32, (T * k,))
+    _want(topk_w, "topk_w", torch.float32, (T, k))
+    if out is not None:
+        _want(out, "out", y.dtype, (T, d))
+    _dev(y, pair_pos, topk_w, out)
     if out is None:
         out = torch.empty((T, d), dtype=y.dtype, device=y.device)
-    _dev(out)
     s = shape(T, d, 8, E, k, e_begin, e_end)
     _check(_load().moe_combine(ctypes.byref(s), _dtype_code(y), _ptr(y), _ptr(pair_pos), _ptr(topk_w),
                                _ptr(out), _stream(stream)), "moe_combine")
@@ -309,6 +452,8 @@ def layer(x, logits, w_gate_up, w_down, k: int, e_begin: int, e_end: int, stream
     as "gu", for layer_backward to use instead of recomputing them."""
     torch = _torch()
     T = x.shape[0]
+    if logits.dim() != 2 or logits.shape[0] != T:
+        raise ValueError(f"logits must be [T={T}, E], got {list(logits.shape)}")
     E = logits.shape[1]
     if save and not fused:
         raise ValueError("save needs the fused path")
@@ -334,8 +479,21 @@ def combine_backward(d_out, y, pair_pos, topk_w, T: int, k: int, E: int, e_begin
                      d_y=None, d_topk_w=None, stream=None):
     """(d_y [N_max, d], d_topk_w [T, k] fp32): the gradient of combine."""
     torch = _torch()
-    _dev(d_out, y, pair_pos, topk_w)
-    d = d_out.shape[1]
+    _range(E, k, e_begin, e_end)
+    n_max = _n_max(T, k, e_begin, e_end)
+    _want(d_out, "d_out", _act_dtypes())
+    if d_out.dim() != 2:
+        raise ValueError(f"d_out must be [T, d], got {list(d_out.shape)}")
+    d = int(d_out.shape[1])
+    _want(d_out, "d_out", d_out.dtype, (T, d))
+    _want(y, "y", d_out.dtype, (n_max, d), min_rows=n_max)
+    _want(pair_pos, "pair_pos", torch.int32, (T * k,))
+    _want(topk_w, "topk_w", torch.float32, (T, k))
+    if d_y is not None:
+        _want(d_y, "d_y", d_out.dtype, (n_max, d), min_rows=n_max)
+    if d_topk_w is not None:
+        _want(d_topk_w, "d_topk_w", torch.float32, (T, k))
+    _dev(d_out, y, pair_pos, topk_w, d_y, d_topk_w)
     if d_y is None:
         d_y = torch.empty_like(y)
     if d_topk_w is None:
@@ -358,20 +516,42 @@ def grouped_gemm_backward(x, perm, offsets, w_gate_up, w_down, h, d_y, k: int, E
     With gu (the pre-activations the saving forward kept) they are not
     recomputed (moe_grouped_gemm_backward_saved)."""
     torch = _torch()
-    _dev(x, perm, offsets, w_gate_up, w_down, h, d_y)
-    T, d = x.shape
-    e_loc, d_ff, _ = w_down.shape
+    _range(E, k, e_begin, e_end)
+    _want(x, "x", _act_dtypes())
+    if x.dim() != 2:
+        raise ValueError(f"x must be [T, d], got {list(x.shape)}")
+    T, d = (int(v) for v in x.shape)
+    n_max = _n_max(T, k, e_begin, e_end)
+    dt_ = x.dtype
+    _want(perm, "perm", torch.int32, (T * k,))
+    _want(offsets, "offsets", torch.int32, (E + 1,))
+    d_ff = _expert_weights(w_gate_up, w_down, dt_, d, e_begin, e_end)
+    _want(h, "h", dt_, (n_max, d_ff), min_rows=n_max)
+    _want(d_y, "d_y", dt_, (n_max, d), min_rows=n_max)
+    if d_x_perm is not None:
+        _want(d_x_perm, "d_x_perm", dt_, (n_max, d), min_rows=n_max)
+    if d_w_gate_up is not None:
+        _want(d_w_gate_up, "d_w_gate_up", dt_, tuple(w_gate_up.shape))
+    if d_w_down is not None:
+        _want(d_w_down, "d_w_down", dt_, tuple(w_down.shape))
+    if gu is not None:
+        _want(gu, "gu", dt_, (n_max, 2 * d_ff), min_rows=n_max)
     s = shape(T, d, d_ff, E, k, e_begin, e_end)
     dt = _dtype_code(x)
+    ws_bytes = int(_load().moe_grouped_gemm_backward_workspace_bytes(ctypes.byref(s), dt))
+    if workspace is not None:
+        _want(workspace, "workspace", torch.uint8)
+        if workspace.numel() < ws_bytes:
+            raise ValueError(f"workspace must hold at least {ws_bytes} bytes, got {workspace.numel()}")
+    _dev(x, perm, offsets, w_gate_up, w_down, h, d_y, d_x_perm, d_w_gate_up, d_w_down, gu, workspace)
     if d_x_perm is None:
-        d_x_perm = torch.empty_like(d_y)
+        d_x_perm = torch.empty((n_max, d), dtype=dt_, device=x.device)
     if d_w_gate_up is None:
         d_w_gate_up = torch.empty_like(w_gate_up)
     if d_w_down is None:
         d_w_down = torch.empty_like(w_down)
     ws = workspace
     if ws is None:
-        ws_bytes = _load().moe_grouped_gemm_backward_workspace_bytes(ctypes.byref(s), dt)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device) if ws_bytes else None
     if gu is None:
         _check(_load().moe_grouped_gemm_backward(ctypes.byref(s), dt, _ptr(x), _ptr(perm), _ptr(offsets),
@@ -379,9 +559,6 @@ def grouped_gemm_backward(x, perm, offsets, w_gate_up, w_down, h, d_y, k: int, E
                                                  _ptr(d_w_gate_up), _ptr(d_w_down), _ptr(ws), _stream(stream)),
                "moe_grouped_gemm_backward")
     else:
-        _dev(gu)
-        if tuple(gu.shape) != (h.shape[0], 2 * d_ff) or gu.dtype != h.dtype:
-            raise ValueError("gu must be [N_max, 2*d_ff] in the activations' dtype")
         _check(_load().moe_grouped_gemm_backward_saved(ctypes.byref(s), dt, _ptr(x), _ptr(perm), _ptr(offsets),
                                                        _ptr(w_gate_up), _ptr(w_down), _ptr(h), _ptr(gu), _ptr(d_y),
                                                        _ptr(d_x_perm), _ptr(d_w_gate_up), _ptr(d_w_down), _ptr(ws),
@@ -392,8 +569,17 @@ def grouped_gemm_backward(x, perm, offsets, w_gate_up, w_down, h, d_y, k: int, E
 def dispatch_backward(d_x_perm, pair_pos, T: int, k: int, E: int, e_begin: int, e_end: int, d_x=None, stream=None):
     """d_x [T, d]: the gradient of the row gather."""
     torch = _torch()
-    _dev(d_x_perm, pair_pos)
-    d = d_x_perm.shape[1]
+    _range(E, k, e_begin, e_end)
+    n_max = _n_max(T, k, e_begin, e_end)
+    _want(d_x_perm, "d_x_perm", _act_dtypes())
+    if d_x_perm.dim() != 2:
+        raise ValueError(f"d_x_perm must be [N_max, d], got {list(d_x_perm.shape)}")
+    d = int(d_x_perm.shape[1])
+    _want(d_x_perm, "d_x_perm", d_x_perm.dtype, (n_max, d), min_rows=n_max)
+    _want(pair_pos, "pair_pos", torch.int32, (T * k,))
+    if d_x is not None:
+        _want(d_x, "d_x", d_x_perm.dtype, (T, d))
+    _dev(d_x_perm, pair_pos, d_x)
     if d_x is None:
         d_x = torch.empty((T, d), dtype=d_x_perm.dtype, device=d_x_perm.device)
     s = shape(T, d, 8, E, k, e_begin, e_end)
@@ -405,8 +591,17 @@ def dispatch_backward(d_x_perm, pair_pos, T: int, k: int, E: int, e_begin: int, 
 def route_topk_backward(topk_idx, topk_w, d_topk_w, E: int, d_logits=None, stream=None):
     """d_logits [T, E] fp32: the gradient of route_topk's weights w.r.t. the logits."""
     torch = _torch()
-    _dev(topk_idx, topk_w, d_topk_w)
-    T, k = topk_idx.shape
+    _want(topk_idx, "topk_idx", torch.int32)
+    if topk_idx.dim() != 2:
+        raise ValueError(f"topk_idx must be [T, k], got {list(topk_idx.shape)}")
+    T, k = (int(v) for v in topk_idx.shape)
+    if not 1 <= k <= E:
+        raise ValueError(f"need 1 <= k <= E, got k={k}, E={E}")
+    _want(topk_w, "topk_w", torch.float32, (T, k))
+    _want(d_topk_w, "d_topk_w", torch.float32, (T, k))
+    if d_logits is not None:
+        _want(d_logits, "d_logits", torch.float32, (T, E))
+    _dev(topk_idx, topk_w, d_topk_w, d_logits)
     if d_logits is None:
         d_logits = torch.empty((T, E), dtype=torch.float32, device=topk_idx.device)
     s = shape(T, 8, 8, E, k, 0, E)

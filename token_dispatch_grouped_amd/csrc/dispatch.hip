@@ -29,12 +29,24 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Debug builds (MOE_DEBUG defined) also count the ids outside [0, E): an extra
+// histogram row E (bucket E) whose total is the error word at the start of the
+// workspace. Release builds drop such ids without counting them.
+#ifdef MOE_DEBUG
+constexpr int kDebugRows = 1;
+#else
+constexpr int kDebugRows = 0;
+#endif
+// ints before the histogram tables: the debug error word, padded to 256 bytes
+constexpr int kWsHead = kDebugRows * 64;
+
 template <int CHUNK>
 __global__ __launch_bounds__(kThreads) void dispatch_count_kernel(const int32_t* __restrict__ idx,
                                                                   int32_t* __restrict__ ws,
                                                                   int64_t P, int E, int n_chunks) {
-  __shared__ int hist[kMaxExperts];
-  for (int e = threadIdx.x; e < E; e += kThreads) hist[e] = 0;
+  __shared__ int hist[kMaxExperts + kDebugRows];
+  const int rows = E + kDebugRows;
+  for (int e = threadIdx.x; e < rows; e += kThreads) hist[e] = 0;
   __syncthreads();
   const int64_t base = static_cast<int64_t>(blockIdx.x) * CHUNK;
   for (int i = threadIdx.x; i < CHUNK; i += kThreads) {
@@ -42,10 +54,11 @@ __global__ __launch_bounds__(kThreads) void dispatch_count_kernel(const int32_t*
     if (p < P) {
       const int e = idx[p];
       if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&hist[e], 1);
+      else if (kDebugRows) atomicAdd(&hist[E], 1);
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kThreads)
+  for (int e = threadIdx.x; e < rows; e += kThreads)
     ws[static_cast<int64_t>(e) * n_chunks + blockIdx.x] = hist[e];
 }
 
@@ -60,25 +73,33 @@ constexpr int kScanWavesPerBlock = kThreads / kWave;
 //           a scatter workgroup reads its E bases as one contiguous row.
 //           Workgroup 0 also writes counts and offsets.
 __global__ __launch_bounds__(kThreads) void dispatch_zero_counts_kernel(int32_t* __restrict__ counts,
-                                                                        int32_t* __restrict__ offsets, int E) {
+                                                                        int32_t* __restrict__ offsets,
+                                                                        int32_t* __restrict__ err_word, int E) {
   for (int e = threadIdx.x; e <= E; e += kThreads) {
     if (e < E) counts[e] = 0;
     offsets[e] = 0;
   }
+  if (kDebugRows && threadIdx.x == 0) err_word[0] = 0;
 }
 
+// `rows` is E, or E + 1 in debug builds (the last total is the count of ids
+// outside [0, E), and also goes to the error word).
 __global__ __launch_bounds__(kThreads) void dispatch_totals_kernel(const int32_t* __restrict__ ws,
-                                                                   int32_t* __restrict__ tot, int E,
+                                                                   int32_t* __restrict__ tot,
+                                                                   int32_t* __restrict__ err_word, int E,
                                                                    int n_chunks) {
   const int lane = lane_id();
   const int e = blockIdx.x * kScanWavesPerBlock + threadIdx.x / kWave;
-  if (e >= E) return;
+  if (e >= E + kDebugRows) return;
   const int32_t* row = ws + static_cast<int64_t>(e) * n_chunks;
   int s = 0;
   for (int c = lane; c < n_chunks; c += kWave) s += row[c];
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
-  if (lane == 0) tot[e] = s;
+  if (lane == 0) {
+    tot[e] = s;
+    if (kDebugRows && e == E) err_word[0] = s;
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void dispatch_bases_kernel(const int32_t* __restrict__ ws,
@@ -228,7 +249,8 @@ constexpr int kSmallPairs = 2048;
 
 __global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(
     const int32_t* __restrict__ idx, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ perm, int32_t* __restrict__ pair_pos, int P, int E, int e_begin, int e_end) {
+    int32_t* __restrict__ perm, int32_t* __restrict__ pair_pos, int32_t* __restrict__ err_word, int P, int E,
+    int e_begin, int e_end) {
   constexpr int kWaves = kSmallThreads / kWave;
   constexpr int kPasses = kSmallPairs / kSmallThreads;
   __shared__ int run[kMaxExperts + 1];        // histogram, then the next sorted slot of each expert
@@ -243,12 +265,17 @@ __global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(
     const int p = pass * kSmallThreads + tid;
     ids[pass] = p < P ? idx[p] : -1;
   }
+  __shared__ int bad;  // ids outside [0, E) (debug builds)
   for (int e = tid; e < E; e += kSmallThreads) run[e] = 0;
+  if (tid == 0) bad = 0;
   __syncthreads();
 #pragma unroll
-  for (int pass = 0; pass < kPasses; ++pass)
+  for (int pass = 0; pass < kPasses; ++pass) {
     if (static_cast<unsigned>(ids[pass]) < static_cast<unsigned>(E)) atomicAdd(&run[ids[pass]], 1);
+    else if (kDebugRows && pass * kSmallThreads + tid < P) atomicAdd(&bad, 1);
+  }
   __syncthreads();
+  if (kDebugRows && tid == 0) err_word[0] = bad;
   if (wv == 0) {  // exclusive scan: counts, offsets, and each expert's first slot
     int carry = 0;
     for (int e0 = 0; e0 < E; e0 += kWave) {
@@ -360,25 +387,31 @@ size_t dispatch_workspace_bytes(int64_t T, int k, int E) {
   const int64_t P = T * k;
   const int chunk = dispatch_chunk(P, E);
   const int64_t n_chunks = (P + chunk - 1) / chunk;
-  if (n_chunks == 0) return 0;
-  // per-(expert, chunk) counts, per-(chunk, expert) first slots, per-expert totals
-  return (2 * static_cast<size_t>(n_chunks * E) + E) * sizeof(int32_t);
+  const int64_t rows = E + kDebugRows;
+  if (n_chunks == 0) return kWsHead * sizeof(int32_t);
+  // (debug: the error word), per-(expert, chunk) counts, per-(chunk, expert) first slots, per-expert totals
+  return (kWsHead + static_cast<size_t>(n_chunks * rows) + static_cast<size_t>(n_chunks * E) + rows) *
+         sizeof(int32_t);
 }
+
+size_t dispatch_debug_word_offset() { return kDebugRows ? 0 : SIZE_MAX; }
 
 hipError_t launch_dispatch(const void* x, size_t row_bytes, const int32_t* idx, int32_t* counts,
                            int32_t* offsets, int32_t* perm, int32_t* pair_pos, void* x_perm,
                            void* workspace, int64_t T, int k, int E, int e_begin, int e_end,
                            int64_t n_max, hipStream_t stream) {
   const int64_t P = T * k;
+  int32_t* err_word = static_cast<int32_t*>(workspace);  // read by the kernels in debug builds only
   if (P > 0 && P <= kSmallPairs) {
     hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(kSmallThreads), 0, stream, idx, counts, offsets, perm,
-                       pair_pos, static_cast<int>(P), E, e_begin, e_end);
+                       pair_pos, err_word, static_cast<int>(P), E, e_begin, e_end);
     if (x_perm == nullptr) return hipGetLastError();
     return launch_gather_rows(x, row_bytes, perm, offsets, x_perm, k, e_begin, e_end, n_max, stream);
   }
   const int chunk = dispatch_chunk(P, E);
   const int n_chunks = static_cast<int>((P + chunk - 1) / chunk);
-  int32_t* ws = static_cast<int32_t*>(workspace);
+  const int rows = E + kDebugRows;
+  int32_t* ws = static_cast<int32_t*>(workspace) + kWsHead;
   if (n_chunks > 0) {
     if (chunk == 256)
       hipLaunchKernelGGL(dispatch_count_kernel<256>, dim3(n_chunks), dim3(kThreads), 0, stream, idx, ws, P, E,
@@ -387,15 +420,18 @@ hipError_t launch_dispatch(const void* x, size_t row_bytes, const int32_t* idx, 
       hipLaunchKernelGGL(dispatch_count_kernel<1024>, dim3(n_chunks), dim3(kThreads), 0, stream, idx, ws, P, E,
                          n_chunks);
   }
-  int32_t* bases = ws + static_cast<int64_t>(n_chunks) * E;
+  int32_t* bases = ws + static_cast<int64_t>(n_chunks) * rows;
   int32_t* tot = bases + static_cast<int64_t>(n_chunks) * E;
   const int scan_blocks = (E + kScanWavesPerBlock - 1) / kScanWavesPerBlock;
   if (n_chunks == 0) {
     // no pairs: counts and offsets are all zero (tot is the E zeros the totals pass would give)
-    hipLaunchKernelGGL(dispatch_zero_counts_kernel, dim3(1), dim3(kThreads), 0, stream, counts, offsets, E);
+    hipLaunchKernelGGL(dispatch_zero_counts_kernel, dim3(1), dim3(kThreads), 0, stream, counts, offsets, err_word,
+                       E);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(dispatch_totals_kernel, dim3(scan_blocks), dim3(kThreads), 0, stream, ws, tot, E, n_chunks);
+  const int total_blocks = (rows + kScanWavesPerBlock - 1) / kScanWavesPerBlock;
+  hipLaunchKernelGGL(dispatch_totals_kernel, dim3(total_blocks), dim3(kThreads), 0, stream, ws, tot, err_word, E,
+                     n_chunks);
   hipLaunchKernelGGL(dispatch_bases_kernel, dim3(scan_blocks), dim3(kThreads), 0, stream, ws, tot, bases, counts,
                      offsets, E, n_chunks);
   if (chunk == 256)

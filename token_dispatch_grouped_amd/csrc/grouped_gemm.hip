@@ -40,8 +40,6 @@
 //     resource ends at the tile's last valid row.
 //
 // fp32 (small parity workload): a plain VALU tiled kernel with the same tile walk.
-#include <stdlib.h>
-#include <string.h>
 
 #include <atomic>
 
@@ -323,10 +321,8 @@ hipError_t launch_grouped_gemm_bf16(const void* x_perm, const int32_t* offsets, 
   const int g1 = grid_for(n_max, e_loc, kBM, (d_ff + 127) / 128, 1);
   const int g2 = grid_for(n_max, e_loc, kBM, (d + 255) / 256, 1);
   // The LDS-pipelined kernel needs K (d for gate/up, d_ff for down) in whole
-  // 32-wide stages; MOE_GEMM_KERNEL=regs forces the register-staged kernel.
-  const char* force = getenv("MOE_GEMM_KERNEL");
-  const bool regs = force != nullptr && strcmp(force, "regs") == 0;
-  if (!regs && d % 32 == 0 && d_ff % 32 == 0)
+  // 32-wide stages; other multiples of 8 take the register-staged kernel.
+  if (d % 32 == 0 && d_ff % 32 == 0)
     return launch_grouped_gemm_lds(x_perm, nullptr, T, k, offsets, w_gu, w_dn, h, y, nullptr, d, d_ff, e_begin,
                                    e_loc, n_max, g1, g2, stream);
   hipLaunchKernelGGL(grouped_gemm_bf16_kernel<true>, dim3(g1), dim3(kThreads), 0, stream,

@@ -92,12 +92,10 @@ moe_status moe_dispatch(const moe_shape* s, moe_dtype dt, const void* x, const i
   if (st != MOE_OK) return st;
   if (!valid_dtype(dt)) return MOE_EINVAL;
   if (counts == nullptr || offsets == nullptr) return MOE_EINVAL;
-  if (s->T > 0) {
-    if (x == nullptr || topk_idx == nullptr || perm == nullptr || pair_pos == nullptr ||
-        x_perm == nullptr)
-      return MOE_EINVAL;
-    if (moe::dispatch_workspace_bytes(s->T, s->k, s->E) > 0 && workspace == nullptr) return MOE_EINVAL;
-  }
+  if (s->T > 0 && (x == nullptr || topk_idx == nullptr || perm == nullptr || pair_pos == nullptr ||
+                   x_perm == nullptr))
+    return MOE_EINVAL;
+  if (moe::dispatch_workspace_bytes(s->T, s->k, s->E) > 0 && workspace == nullptr) return MOE_EINVAL;
   return from_hip(moe::launch_dispatch(x, static_cast<size_t>(s->d) * elem_bytes(dt), topk_idx, counts,
                                        offsets, perm, pair_pos, x_perm, workspace, s->T, s->k, s->E,
                                        s->e_begin, s->e_end, n_max_of(s), stream));
@@ -108,13 +106,13 @@ moe_status moe_dispatch_indices(const moe_shape* s, const int32_t* topk_idx, int
   const moe_status st = check_shape(s, true);
   if (st != MOE_OK) return st;
   if (counts == nullptr || offsets == nullptr) return MOE_EINVAL;
-  if (s->T > 0) {
-    if (topk_idx == nullptr || perm == nullptr || pair_pos == nullptr) return MOE_EINVAL;
-    if (moe::dispatch_workspace_bytes(s->T, s->k, s->E) > 0 && workspace == nullptr) return MOE_EINVAL;
-  }
+  if (s->T > 0 && (topk_idx == nullptr || perm == nullptr || pair_pos == nullptr)) return MOE_EINVAL;
+  if (moe::dispatch_workspace_bytes(s->T, s->k, s->E) > 0 && workspace == nullptr) return MOE_EINVAL;
   return from_hip(moe::launch_dispatch(nullptr, 0, topk_idx, counts, offsets, perm, pair_pos, nullptr, workspace,
                                        s->T, s->k, s->E, s->e_begin, s->e_end, n_max_of(s), stream));
 }
+
+size_t moe_dispatch_debug_word_offset(void) { return moe::dispatch_debug_word_offset(); }
 
 size_t moe_grouped_gemm_workspace_bytes(const moe_shape* s, moe_dtype dt) {
   (void)s;

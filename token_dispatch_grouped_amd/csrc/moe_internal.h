@@ -52,6 +52,8 @@ hipError_t launch_route_topk(const float* logits, int32_t* idx, float* w, int64_
                              hipStream_t stream);
 
 size_t dispatch_workspace_bytes(int64_t T, int k, int E);
+// byte offset of the debug error word in the dispatch workspace; SIZE_MAX in release builds
+size_t dispatch_debug_word_offset();
 hipError_t launch_dispatch(const void* x, size_t row_bytes, const int32_t* idx, int32_t* counts,
                            int32_t* offsets, int32_t* perm, int32_t* pair_pos, void* x_perm,
                            void* workspace, int64_t T, int k, int E, int e_begin, int e_end,
