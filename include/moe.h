@@ -13,8 +13,10 @@
  *     the caller allocates and owns. The library allocates nothing. Its only
  *     process-wide state is a per-device cache of the compute-unit count (read
  *     once per device with hipDeviceGetAttribute, filled atomically, never
- *     changed afterwards), which sizes the persistent GEMM grids. Calls on
- *     different streams may run concurrently when they write disjoint buffers.
+ *     changed afterwards), which sizes the persistent GEMM grids, and the
+ *     per-device array of moe_dispatch_indices_noalloc with its address cache.
+ *     Calls on different streams may run concurrently when they write disjoint
+ *     buffers (moe_dispatch_indices_noalloc excepted: see there).
  *   - Every call validates its arguments on the host, enqueues its kernels on
  *     `stream` and returns without synchronising. Invalid arguments return
  *     MOE_EINVAL (or MOE_EUNSUPPORTED for a valid but unsupported shape) before
@@ -140,6 +142,24 @@ size_t moe_dispatch_debug_word_offset(void);
 moe_status moe_dispatch_indices(const moe_shape* s, const int32_t* topk_idx,
                                 int32_t* counts, int32_t* offsets, int32_t* perm,
                                 int32_t* pair_pos, void* workspace, hipStream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): moe_dispatch_indices
+ * with its workspace taken from an array of MOE_DISPATCH_SCRATCH_BYTES bytes
+ * that the library holds in each GPU's device memory until the process ends.
+ * Same outputs, bit for bit, and same errors as moe_dispatch_indices, plus
+ * MOE_EUNSUPPORTED when moe_dispatch_workspace_bytes(s) exceeds
+ * MOE_DISPATCH_SCRATCH_BYTES (8 MiB: for example up to about 1M pairs at
+ * E = 256, or 2M pairs at E = 128), and MOE_EHIP if the array's address cannot
+ * be found. No memory is allocated or freed. Every call on one GPU uses that
+ * GPU's one array, so calls that overlap on one GPU (from several streams or
+ * host threads) race and give undefined results; calls in one stream are safe.
+ * The array needs no clearing between calls. The stream must belong to the
+ * current device. */
+#define MOE_DISPATCH_SCRATCH_BYTES ((size_t)8 << 20)
+moe_status moe_dispatch_indices_noalloc(const moe_shape* s, const int32_t* topk_idx,
+                                        int32_t* counts, int32_t* offsets, int32_t* perm,
+                                        int32_t* pair_pos, hipStream_t stream);
 
 /* Bytes of device workspace moe_grouped_gemm needs for this shape (may be 0). */
 size_t moe_grouped_gemm_workspace_bytes(const moe_shape* s, moe_dtype dt);

@@ -220,3 +220,16 @@ def test_debug_library_exports_every_declared_symbol_and_has_the_error_word():
     finally:
         moe.set_debug(False)
     assert moe.dispatch_workspace_bytes(0, 2, 8) == 0
+
+
+def test_noalloc_dispatch_refuses_shapes_past_its_array():
+    lib = moe.lib()
+    big = _shape(T=1 << 20, k=8, E=256, e_begin=0, e_end=32)  # 8M pairs: a 64 MiB workspace
+    assert moe.lib().moe_dispatch_workspace_bytes(ctypes.byref(big)) > 8 << 20
+    assert lib.moe_dispatch_indices_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == \
+        moe.MOE_EUNSUPPORTED
+    s = _shape()
+    assert lib.moe_dispatch_indices_noalloc(ctypes.byref(s), FAKE, NULL, FAKE, FAKE, FAKE, NULL) == moe.MOE_EINVAL
+    assert lib.moe_dispatch_indices_noalloc(ctypes.byref(s), NULL, FAKE, FAKE, FAKE, FAKE, NULL) == moe.MOE_EINVAL
+    assert lib.moe_dispatch_indices_noalloc(ctypes.byref(_shape(k=9)), FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == \
+        moe.MOE_EINVAL

@@ -83,6 +83,7 @@ def _load():
             "moe_dispatch_debug_word_offset": (SZ, []),
             "moe_dispatch": (ctypes.c_int, [S, ctypes.c_int, P, P, P, P, P, P, P, P, P]),
             "moe_dispatch_indices": (ctypes.c_int, [S, P, P, P, P, P, P, P]),
+            "moe_dispatch_indices_noalloc": (ctypes.c_int, [S, P, P, P, P, P, P]),
             "moe_grouped_gemm_gather": (ctypes.c_int, [S, ctypes.c_int, P, P, P, P, P, P, P, P, P]),
             "moe_grouped_gemm_workspace_bytes": (SZ, [S, ctypes.c_int]),
             "moe_grouped_gemm": (ctypes.c_int, [S, ctypes.c_int, P, P, P, P, P, P, P, P]),
@@ -346,6 +347,28 @@ def dispatch(x, topk_idx, E: int, e_begin: int, e_end: int, out: Dispatch | None
     if _debug:
         _debug_word(out, E, stream)
     return out
+
+
+def dispatch_indices_noalloc(topk_idx, E: int, e_begin: int, e_end: int, counts, offsets, perm, pair_pos,
+                             stream=None) -> None:
+    """moe_dispatch_indices_noalloc: the dispatch's indices into caller-provided
+    buffers, with the library's per-GPU array as workspace (nothing allocated;
+    calls that overlap on one GPU race)."""
+    torch = _torch()
+    _want(topk_idx, "topk_idx", torch.int32)
+    if topk_idx.dim() != 2:
+        raise ValueError(f"topk_idx must be [T, k], got {list(topk_idx.shape)}")
+    T, k = (int(v) for v in topk_idx.shape)
+    _range(E, k, e_begin, e_end)
+    _want(counts, "counts", torch.int32, (E,))
+    _want(offsets, "offsets", torch.int32, (E + 1,))
+    _want(perm, "perm", torch.int32, (T * k,))
+    _want(pair_pos, "pair_pos", torch.int32, (T * k,))
+    _dev(topk_idx, counts, offsets, perm, pair_pos)
+    s = shape(T, 8, 8, E, k, e_begin, e_end)
+    _check(_load().moe_dispatch_indices_noalloc(ctypes.byref(s), _ptr(topk_idx), _ptr(counts), _ptr(offsets),
+                                                _ptr(perm), _ptr(pair_pos), _stream(stream)),
+           "moe_dispatch_indices_noalloc")
 
 
 def _gemm_outputs(h, y, n_max: int, d: int, d_ff: int, dtype, device):

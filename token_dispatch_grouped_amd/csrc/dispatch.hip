@@ -22,6 +22,8 @@
 //                the order inside an expert is the flat-pair order (stable).
 //   4. gather  : one wave per part of a local row copies x[token] into x_perm with 16-byte
 //                loads and stores; the row count is read on the device.
+#include <mutex>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -395,6 +397,31 @@ size_t dispatch_workspace_bytes(int64_t T, int k, int E) {
 }
 
 size_t dispatch_debug_word_offset() { return kDebugRows ? 0 : SIZE_MAX; }
+
+// Workspace of the allocation-free dispatch: one array in each GPU's copy of
+// the code object, held until the process ends. Every call on a GPU shares it.
+static __device__ __align__(256) int32_t scratch[kDispatchScratchBytes / sizeof(int32_t)];
+
+hipError_t dispatch_scratch(void** ptr) {
+  // The array's device address on each GPU, looked up once per device with that
+  // device current (the host-side name is not a device address).
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_dispatch(const void* x, size_t row_bytes, const int32_t* idx, int32_t* counts,
                            int32_t* offsets, int32_t* perm, int32_t* pair_pos, void* x_perm,

@@ -114,6 +114,19 @@ moe_status moe_dispatch_indices(const moe_shape* s, const int32_t* topk_idx, int
 
 size_t moe_dispatch_debug_word_offset(void) { return moe::dispatch_debug_word_offset(); }
 
+moe_status moe_dispatch_indices_noalloc(const moe_shape* s, const int32_t* topk_idx, int32_t* counts,
+                                        int32_t* offsets, int32_t* perm, int32_t* pair_pos, hipStream_t stream) {
+  const moe_status st = check_shape(s, true);
+  if (st != MOE_OK) return st;
+  if (counts == nullptr || offsets == nullptr) return MOE_EINVAL;
+  if (s->T > 0 && (topk_idx == nullptr || perm == nullptr || pair_pos == nullptr)) return MOE_EINVAL;
+  if (moe::dispatch_workspace_bytes(s->T, s->k, s->E) > moe::kDispatchScratchBytes) return MOE_EUNSUPPORTED;
+  void* ws = nullptr;
+  if (moe::dispatch_scratch(&ws) != hipSuccess) return MOE_EHIP;
+  return from_hip(moe::launch_dispatch(nullptr, 0, topk_idx, counts, offsets, perm, pair_pos, nullptr, ws, s->T,
+                                       s->k, s->E, s->e_begin, s->e_end, n_max_of(s), stream));
+}
+
 size_t moe_grouped_gemm_workspace_bytes(const moe_shape* s, moe_dtype dt) {
   (void)s;
   (void)dt;

@@ -54,6 +54,9 @@ hipError_t launch_route_topk(const float* logits, int32_t* idx, float* w, int64_
 size_t dispatch_workspace_bytes(int64_t T, int k, int E);
 // byte offset of the debug error word in the dispatch workspace; SIZE_MAX in release builds
 size_t dispatch_debug_word_offset();
+// the allocation-free dispatch's per-GPU workspace: its size, and its device address on the current device
+constexpr size_t kDispatchScratchBytes = MOE_DISPATCH_SCRATCH_BYTES;
+hipError_t dispatch_scratch(void** ptr);
 hipError_t launch_dispatch(const void* x, size_t row_bytes, const int32_t* idx, int32_t* counts,
                            int32_t* offsets, int32_t* perm, int32_t* pair_pos, void* x_perm,
                            void* workspace, int64_t T, int k, int E, int e_begin, int e_end,
