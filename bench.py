@@ -5,9 +5,11 @@ dispatch -> grouped GEMM (gate/up + SwiGLU, then down) -> combine, through the
 C ABI, with every buffer allocated before timing. Prints ONE JSON line.
 
 Timing: W warm-up steps, then K timed steps, each bracketed by events on the
-stream the kernels run on, with a write of at least 512 MiB to a scratch buffer
-before each step and outside its events, so the 4 MB L2s and the 256 MB
-Infinity Cache hold none of the step's inputs when it starts. The K steps are
+stream the kernels run on. Before each step, outside its events, 512 MiB are
+written to one scratch buffer and then 512 MiB of another are read, so the 4 MB
+L2s and the 256 MB Infinity Cache hold none of the step's inputs when it starts
+(the read pass also writes back the dirty lines the write left, which would
+otherwise be written back during the step). The K steps are
 bracketed by a device synchronisation on both sides; `value` and `ms_per_step`
 use the median of the per-step event times. The same K steps back to back, with
 no flush, give `back_to_back_ms_per_step` (wall clock) for comparison.
@@ -173,8 +175,10 @@ def main() -> int:
                     help="after timing, repeat the step for this many seconds while sampling the "
                          "shader clock with rocm-smi; reports the median as sclk_mhz")
     ap.add_argument("--flush-mib", type=int, default=512,
-                    help="MiB written to a scratch buffer before each timed step, outside its events "
-                         "(0: no flush)")
+                    help="MiB written to one scratch buffer, then read from another, before each timed "
+                         "step and outside its events (0: no flush)")
+    ap.add_argument("--flush-mode", choices=["write-read", "write", "read"], default="write-read",
+                    help="which flush passes run before each timed step")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (3 times), the "
                          "reference for scaling FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -233,6 +237,17 @@ def main() -> int:
                for _ in range(args.steps)]
     flush_buf = (torch.empty(args.flush_mib << 18, dtype=torch.float32, device=dev)
                  if args.flush_mib > 0 else None)
+    flush_src = (torch.ones(args.flush_mib << 18, dtype=torch.float32, device=dev)
+                 if args.flush_mib > 0 else None)
+    flush_sink = torch.zeros((), dtype=torch.float32, device=dev)
+
+    def flush(i):
+        if flush_buf is None:
+            return
+        if args.flush_mode != "read":
+            flush_buf.fill_(float(i + 1))
+        if args.flush_mode != "write":
+            torch.sum(flush_src, dim=0, out=flush_sink)
 
     gu = None  # training: the gate/up pre-activations the forward keeps for the backward
 
@@ -321,8 +336,7 @@ def main() -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        if flush_buf is not None:
-            flush_buf.fill_(float(i))
+        flush(i)
         ev_step[i][0].record(cur())
         if graph is not None:
             graph.replay()
@@ -335,8 +349,7 @@ def main() -> int:
     ms_step = float(np.median(step_ms))
     if graph is not None:  # the GEMM's events come from an eager pass after the timed replays
         for i in range(args.steps):
-            if flush_buf is not None:
-                flush_buf.fill_(float(i))
+            flush(i)
             step(i)
         torch.cuda.synchronize()
     gemm_all = [a.elapsed_time(b) for a, b in ev]
@@ -410,7 +423,7 @@ def main() -> int:
                    "step": "forward + backward" if args.train else "forward"},
         "local_pairs_per_s": round(n_loc / (ms_step * 1e-3), 1),
         "timing": {"per_step": f"median of {args.steps} per-step event times, each step after a "
-                               f"{args.flush_mib} MiB flush write outside its events",
+                               f"{args.flush_mib} MiB flush ({args.flush_mode}) outside its events",
                    "step_ms_min": round(float(np.min(step_ms)), 4),
                    "step_ms_max": round(float(np.max(step_ms)), 4),
                    "wall_ms_per_step_incl_flush": round(wall_flushed_ms, 4),

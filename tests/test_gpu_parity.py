@@ -398,26 +398,25 @@ def test_decode_shaped_skewed_layer_matches_oracle(w):
     assert torch.equal(fused["out"], res["out"])
 
 
-@pytest.mark.parametrize("T,k,E,lo,hi", [(600000, 8, 256, 0, 32), (4096, 8, 256, 0, 32), (70000, 4, 128, 16, 32)],
-                         ids=["chunks_of_1024", "chunks_of_256", "chunks_of_256_ragged"])
-def test_dispatch_both_chunk_sizes(T, k, E, lo, hi):
-    """The dispatch switches from 256-pair to 1024-pair chunks once its (expert,
-    chunk) tables would pass 4M entries; both give the stable permutation."""
+@pytest.mark.parametrize("T,k,E,lo,hi", [(600000, 8, 256, 0, 32), (16384, 8, 256, 0, 32), (70000, 4, 128, 16, 32),
+                                         (4096, 8, 256, 0, 32), (8193, 8, 1024, 1000, 1024), (257, 8, 16, 0, 8)],
+                         ids=["four_launches_chunks_of_1024", "four_launches_chunks_of_256",
+                              "four_launches_chunks_of_256_ragged", "one_launch", "one_launch_largest",
+                              "one_launch_smallest"])
+def test_dispatch_every_path(T, k, E, lo, hi):
+    """Every dispatch path gives the oracle's stable permutation: one launch per
+    1024 pairs up to 65536 pairs (above the single-workgroup 2048), then four
+    launches with 256-pair chunks, switching to 1024-pair chunks once the
+    (expert, chunk) tables would pass 4M entries."""
     rng = np.random.default_rng(T + k + E)
     idx_np = rng.integers(0, E, size=(T, k)).astype(np.int32)
     x = torch.empty((T, 8), dtype=torch.bfloat16, device="cuda")
     disp = moe.dispatch(x, torch.from_numpy(idx_np).cuda(), E, lo, hi, gather=False)
     torch.cuda.synchronize()
-    flat = idx_np.reshape(-1)
-    counts = np.bincount(flat, minlength=E)
-    offsets = np.concatenate([[0], np.cumsum(counts)])
-    perm = np.argsort(flat, kind="stable")
+    counts, offsets, perm, pair_pos, _ = oracle.dispatch(idx_np, E, lo, hi, np.zeros((T, 0)))
     np.testing.assert_array_equal(disp.counts.cpu().numpy(), counts)
     np.testing.assert_array_equal(disp.offsets.cpu().numpy(), offsets)
     np.testing.assert_array_equal(disp.perm.cpu().numpy(), perm)
-    seg0, seg1 = offsets[lo], offsets[hi]
-    pair_pos = np.full(T * k, -1)
-    pair_pos[perm[seg0:seg1]] = np.arange(seg1 - seg0)
     np.testing.assert_array_equal(disp.pair_pos.cpu().numpy(), pair_pos)
 
 
@@ -463,7 +462,8 @@ def test_layers_on_two_streams_from_two_threads():
 
 # ----------------------------------------------------------------------------- debug build
 
-@pytest.mark.parametrize("T,E,k", [(300, 8, 2), (3000, 64, 4), (0, 16, 2)], ids=["one_workgroup", "chunked", "empty"])
+@pytest.mark.parametrize("T,E,k", [(300, 8, 2), (3000, 64, 4), (20000, 64, 4), (0, 16, 2)],
+                         ids=["one_workgroup", "one_launch", "four_launches", "empty"])
 def test_debug_build_refuses_out_of_range_ids(T, E, k):
     """libmoe_debug.so counts the ids outside [0, E) on the device and the binding
     refuses them; valid ids give the release build's results bit for bit."""

@@ -6,7 +6,8 @@
 // every token the rank holds): out[t] = sum_j w[t,j] * y[pair_pos[t*k+j]] over
 // the token's local pairs, in slot order, in fp32; zero if it has none.
 //
-// Design: one wave per token (grid-stride). The token's k row indices and
+// Design: one wave per token (grid-stride), or per part of a token's row when
+// the batch is short. The token's k row indices and
 // weights come in with one vector load (a lane per slot); a ballot gives the
 // local slots, visited in slot order through readlane two at a time (both rows'
 // loads in flight together), and a token with none writes its zero row
@@ -59,18 +60,24 @@ struct Vec<false> {  // 4 fp32 per 16 bytes
   }
 };
 
-// kChunks: 16-byte chunks per lane per pass over a row (a pass covers kChunks KB)
+// kChunks: 16-byte chunks per lane per pass over a row (a pass covers kChunks KB).
+// A wave takes one part of a token's row (vectors [cb, ce)): the whole row, or,
+// for short batches, one of `split` parts of `span` vectors.
 template <bool BF16, bool UNIT, int kChunks>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const uint4* __restrict__ y,
                                                            const int32_t* __restrict__ pair_pos,
                                                            const float* __restrict__ w,
                                                            uint4* __restrict__ out, int64_t T, int k,
-                                                           int row_vec, int64_t n_max) {
+                                                           int row_vec, int64_t n_max, int split, int span) {
   using V = Vec<BF16>;
   const int lane = lane_id();
   const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kThreads / kWave);
-  for (int64_t t = uniform(static_cast<int>(blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave)); t < T;
-       t += nwaves) {
+  const int64_t items = T * split;
+  for (int64_t it = uniform(static_cast<int>(blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave)); it < items;
+       it += nwaves) {
+    const int64_t t = it / split;
+    const int cb = static_cast<int>(it - t * split) * span;
+    const int ce = min(row_vec, cb + span);
     // slots j0..j0+63 of this token, one per lane; local ones are visited in slot order
     const int64_t pbase = t * k;
     bool any = false;
@@ -81,13 +88,13 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint4* __restri
     }
     uint4* dst = out + t * row_vec;
     if (!any) {
-      for (int c = lane; c < row_vec; c += kWave) dst[c] = make_uint4(0, 0, 0, 0);
+      for (int c = cb + lane; c < ce; c += kWave) dst[c] = make_uint4(0, 0, 0, 0);
       continue;
     }
-    for (int c0 = 0; c0 < row_vec; c0 += kChunks * kWave) {
-      // buffers over this block of kChunks * kWave vectors of a row: lanes past the
-      // row end load zero and their stores are dropped, with no branch
-      const uint32_t bytes = static_cast<uint32_t>(min(kChunks * kWave, row_vec - c0)) * 16u;
+    for (int c0 = cb; c0 < ce; c0 += kChunks * kWave) {
+      // buffers over this block of kChunks * kWave vectors of the part: lanes past
+      // its end load zero and their stores are dropped, with no branch
+      const uint32_t bytes = static_cast<uint32_t>(min(kChunks * kWave, ce - c0)) * 16u;
       float acc[kChunks][V::kN];
 #pragma unroll
       for (int q = 0; q < kChunks; ++q)
@@ -156,17 +163,24 @@ hipError_t launch_combine(const void* y, const int32_t* pair_pos, const float* w
                           int64_t T, int k, int d, int64_t n_max, bool bf16, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const int row_vec = bf16 ? d / 8 : d / 4;
-  int64_t blocks = (T + (kThreads / kWave) - 1) / (kThreads / kWave);
-  if (blocks > 4096) blocks = 4096;
   // Chunks per lane and pass, by row length (measured, one box, timing each in the
   // layer): rows of more than 8 KB take 8 (skew256's 14 KB rows: 45 us, against
   // 49 with 4 and 56 with 2); 6-8 KB rows take 4 (dense8: 18.7 us against 20.2
   // with 8); shorter rows take 2 (ep8_share128's 5.6 KB: 15.7 us against 17.5):
   // fewer registers, so more of the token waves are resident at once.
   const int chunks = row_vec > 512 ? 8 : row_vec > 384 ? 4 : 2;
+  // A short batch (decode) has too few token waves to keep the memory system
+  // busy, so its rows are cut into one part per pass, a wave each (decode256:
+  // 10.4 -> 7.3 us, decode32 10.2 -> 7.1; dense8's 4096 tokens measured 2 %
+  // slower cut, ep8_share128's 8192 the same).
+  const int passes = (row_vec + chunks * kWave - 1) / (chunks * kWave);
+  const int split = T * passes <= 4096 ? passes : 1;
+  const int span = split == 1 ? row_vec : chunks * kWave;
+  int64_t blocks = (T * split + (kThreads / kWave) - 1) / (kThreads / kWave);
+  if (blocks > 4096) blocks = 4096;
 #define MOE_COMBINE_LAUNCH(B, U, C)                                                                          \
   hipLaunchKernelGGL((combine_kernel<B, U, C>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, \
-                     static_cast<const uint4*>(y), pair_pos, w, static_cast<uint4*>(out), T, k, row_vec, n_max)
+                     static_cast<const uint4*>(y), pair_pos, w, static_cast<uint4*>(out), T, k, row_vec, n_max, split, span)
 #define MOE_COMBINE_CHUNKS(B, U)            \
   if (chunks == 8) MOE_COMBINE_LAUNCH(B, U, 8); \
   else if (chunks == 4) MOE_COMBINE_LAUNCH(B, U, 4); \

@@ -8,7 +8,9 @@
 // pairs are one contiguous segment of the expert-sorted pair list).
 //
 // Design (five small launches, all bounded by the pair count or HBM; a batch of
-// at most 2048 pairs takes one single-workgroup launch instead of 1-3):
+// at most 2048 pairs takes one single-workgroup launch instead of 1-3, and one of
+// at most 65536 pairs one launch of a workgroup per 1024 pairs, each counting
+// every pair itself, then the gather):
 //   1. count   : one workgroup per chunk of 256 (or 1024) flat pairs builds an
 //                LDS histogram and stores it expert-major: ws[e * n_chunks + c].
 //   2. scan    : two launches with one wave per expert: per-expert totals,
@@ -341,6 +343,108 @@ __global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(
   }
 }
 
+// Up to kOnePassPairs pairs (more than one workgroup takes): one launch, one
+// workgroup of 1024 threads per chunk of 1024 pairs. Every workgroup counts all
+// the pairs itself, those before its chunk apart from the rest, so no table of
+// chunk counts has to pass between launches; it scans the counts into offsets
+// and its chunk's first slots, then places its chunk's pairs with the same
+// stable ballot ranking as the other paths (workgroup 0 writes counts and
+// offsets). Each workgroup reads all T*k ids from L2, n_chunks * T*k * 4 bytes in
+// all; past kOnePassPairs the four-launch path reads less.
+constexpr int kOnePassPairs = 65536;
+
+__global__ __launch_bounds__(kSmallThreads) void dispatch_onepass_kernel(
+    const int32_t* __restrict__ idx, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm, int32_t* __restrict__ pair_pos, int32_t* __restrict__ err_word, int P, int E,
+    int e_begin, int e_end) {
+  constexpr int kWaves = kSmallThreads / kWave;
+  constexpr int kUnroll = 8;                  // ids per thread in flight while counting
+  __shared__ int run[kMaxExperts];            // counts before the chunk, then the chunk's next slot per expert
+  __shared__ int rest[kMaxExperts + 1];       // counts from the chunk on, then the offsets
+  __shared__ int wcnt[kWaves][kMaxExperts];   // per-wave counts of the chunk's pass
+  __shared__ int bad;                         // ids outside [0, E) (debug builds)
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wv = tid / kWave;
+  const uint64_t lt_mask = (uint64_t{1} << lane) - 1;
+  const int c0 = blockIdx.x * kSmallThreads;  // the chunk's first pair
+  const int p = c0 + tid;
+  const int e = p < P ? idx[p] : -1;
+  for (int x = tid; x < E; x += kSmallThreads) {
+    run[x] = 0;
+    rest[x] = 0;
+  }
+  if (tid == 0) bad = 0;
+  __syncthreads();
+  for (int b = 0; b < P; b += kSmallThreads * kUnroll) {
+    int ids[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int q = b + u * kSmallThreads + tid;
+      ids[u] = q < P ? idx[q] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int q = b + u * kSmallThreads + tid;
+      if (static_cast<unsigned>(ids[u]) < static_cast<unsigned>(E)) atomicAdd(q < c0 ? &run[ids[u]] : &rest[ids[u]], 1);
+      else if (kDebugRows && q < P) atomicAdd(&bad, 1);
+    }
+  }
+  __syncthreads();
+  if (kDebugRows && blockIdx.x == 0 && tid == 0) err_word[0] = bad;
+  if (wv == 0) {  // counts and their exclusive scan; run[x] becomes the chunk's first slot of expert x
+    int carry = 0;
+    for (int x0 = 0; x0 < E; x0 += kWave) {
+      const int x = x0 + lane;
+      const int before = x < E ? run[x] : 0;
+      const int v = x < E ? before + rest[x] : 0;
+      int incl = v;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      const int first = carry + incl - v;
+      if (x < E) {
+        if (blockIdx.x == 0) {
+          counts[x] = v;
+          offsets[x] = first;
+        }
+        rest[x] = first;
+        run[x] = first + before;
+      }
+      carry += __shfl(incl, kWave - 1);
+    }
+    if (lane == 0) {
+      rest[E] = carry;
+      if (blockIdx.x == 0) offsets[E] = carry;
+    }
+  }
+  for (int i = tid; i < kWaves * E; i += kSmallThreads) wcnt[i / E][i % E] = 0;
+  __syncthreads();
+  const int seg0 = rest[e_begin];
+  const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(E);
+  if (p < P && !valid) pair_pos[p] = -1;
+  uint64_t remaining = __ballot(valid);
+  uint64_t peers = 0;
+  while (remaining) {
+    const int leader = __ffsll(static_cast<unsigned long long>(remaining)) - 1;
+    const int le = __builtin_amdgcn_readlane(e, leader);
+    const uint64_t m = __ballot(valid && e == le);
+    if (valid && e == le) peers = m;
+    remaining &= ~m;
+  }
+  const int rank = __popcll(peers & lt_mask);
+  if (valid && rank == 0) wcnt[wv][e] = __popcll(peers);
+  __syncthreads();
+  if (valid) {
+    int pos = run[e] + rank;
+    for (int w2 = 0; w2 < wv; ++w2) pos += wcnt[w2][e];
+    perm[pos] = p;
+    pair_pos[p] = (e >= e_begin && e < e_end) ? pos - seg0 : -1;
+  }
+}
+
 // Rows are copied in parts of kGatherVec 16-byte vectors (2 per lane), one part
 // per wave at a time, so that a few long rows still spread over many waves. Two
 // per lane, with more parts and waves, measured faster than 4 or 8 on every
@@ -432,6 +536,13 @@ hipError_t launch_dispatch(const void* x, size_t row_bytes, const int32_t* idx, 
   if (P > 0 && P <= kSmallPairs) {
     hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(kSmallThreads), 0, stream, idx, counts, offsets, perm,
                        pair_pos, err_word, static_cast<int>(P), E, e_begin, e_end);
+    if (x_perm == nullptr) return hipGetLastError();
+    return launch_gather_rows(x, row_bytes, perm, offsets, x_perm, k, e_begin, e_end, n_max, stream);
+  }
+  if (P > kSmallPairs && P <= kOnePassPairs) {
+    const int blocks = static_cast<int>((P + kSmallThreads - 1) / kSmallThreads);
+    hipLaunchKernelGGL(dispatch_onepass_kernel, dim3(blocks), dim3(kSmallThreads), 0, stream, idx, counts, offsets,
+                       perm, pair_pos, err_word, static_cast<int>(P), E, e_begin, e_end);
     if (x_perm == nullptr) return hipGetLastError();
     return launch_gather_rows(x, row_bytes, perm, offsets, x_perm, k, e_begin, e_end, n_max, stream);
   }
