@@ -362,6 +362,7 @@ def main() -> int:
             graph.replay()
         else:
             step()
+    host_ms = (time.perf_counter() - t0) * 1e3 / args.steps  # enqueueing only
     torch.cuda.synchronize()
     b2b_ms = (time.perf_counter() - t0) * 1e3 / args.steps
 
@@ -427,7 +428,8 @@ def main() -> int:
                    "step_ms_min": round(float(np.min(step_ms)), 4),
                    "step_ms_max": round(float(np.max(step_ms)), 4),
                    "wall_ms_per_step_incl_flush": round(wall_flushed_ms, 4),
-                   "back_to_back_ms_per_step": round(b2b_ms, 4)},
+                   "back_to_back_ms_per_step": round(b2b_ms, 4),
+                   "back_to_back_host_enqueue_ms_per_step": round(host_ms, 4)},
         "roofline": roofline,
         "cpu_baseline": None,
         "seed": w.seed,

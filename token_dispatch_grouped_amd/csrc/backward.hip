@@ -25,7 +25,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // One wave per token. Per local slot, one pass over the row: d_y gets w * d_out
 // (fp32 product, rounded once), and each lane's part of the dot product is
-// summed in a fixed order, so d_w is deterministic.
+// summed in a fixed order, so d_w is deterministic. bf16 rows move as 16-byte
+// vectors (8 elements per lane and load; d is a multiple of 8), two of them per
+// lane in flight per operand.
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void combine_backward_kernel(
     const void* __restrict__ d_out, const void* __restrict__ y, const int32_t* __restrict__ pair_pos,
@@ -50,18 +52,39 @@ __global__ __launch_bounds__(kThreads) void combine_backward_kernel(
         const float wj = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wl), src));
         float dot = 0.f;
         if (BF16) {
-          const uint16_t* go = static_cast<const uint16_t*>(d_out) + t * d;
-          const uint16_t* yr = static_cast<const uint16_t*>(y) + r * d;
-          uint16_t* dy = static_cast<uint16_t*>(d_y) + r * d;
-          for (int c = 2 * lane; c < d; c += 2 * kWave) {  // d is even: two elements per lane
-            const uint32_t g2 = *reinterpret_cast<const uint32_t*>(go + c);
-            const uint32_t y2 = *reinterpret_cast<const uint32_t*>(yr + c);
-            const float g0 = __uint_as_float(g2 << 16), g1 = __uint_as_float(g2 & 0xFFFF0000u);
-            const float y0 = __uint_as_float(y2 << 16), y1 = __uint_as_float(y2 & 0xFFFF0000u);
-            dot = fmaf(g0, y0, dot);
-            dot = fmaf(g1, y1, dot);
-            *reinterpret_cast<uint32_t*>(dy + c) =
-                static_cast<uint32_t>(f32_to_bf16_rne(wj * g0)) | (static_cast<uint32_t>(f32_to_bf16_rne(wj * g1)) << 16);
+          // 16-byte vectors, kPer per lane per pass; buffers bounded by the row, so
+          // lanes past its end load zeros (adding nothing) and their stores drop
+          constexpr int kPer = 2;
+          const int row_vec = d / 8;
+          const uint4* go = static_cast<const uint4*>(d_out) + t * row_vec;
+          const uint4* yr = static_cast<const uint4*>(y) + r * row_vec;
+          uint4* dy = static_cast<uint4*>(d_y) + r * row_vec;
+          for (int c0 = 0; c0 < row_vec; c0 += kPer * kWave) {
+            const uint32_t bytes = static_cast<uint32_t>(min(kPer * kWave, row_vec - c0)) * 16u;
+            const __amdgpu_buffer_rsrc_t bg = make_rsrc(go + c0, bytes);
+            const __amdgpu_buffer_rsrc_t by = make_rsrc(yr + c0, bytes);
+            const __amdgpu_buffer_rsrc_t bd = make_rsrc(dy + c0, bytes);
+            uint4 gv[kPer], yv[kPer];
+#pragma unroll
+            for (int q = 0; q < kPer; ++q) gv[q] = buffer_load16(bg, static_cast<uint32_t>(q * kWave + lane) * 16u);
+#pragma unroll
+            for (int q = 0; q < kPer; ++q) yv[q] = buffer_load16(by, static_cast<uint32_t>(q * kWave + lane) * 16u);
+#pragma unroll
+            for (int q = 0; q < kPer; ++q) {
+              const uint32_t g4[4] = {gv[q].x, gv[q].y, gv[q].z, gv[q].w};
+              const uint32_t y4[4] = {yv[q].x, yv[q].y, yv[q].z, yv[q].w};
+              uint32_t o4[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float g0 = __uint_as_float(g4[i] << 16), g1 = __uint_as_float(g4[i] & 0xFFFF0000u);
+                const float y0 = __uint_as_float(y4[i] << 16), y1 = __uint_as_float(y4[i] & 0xFFFF0000u);
+                dot = fmaf(g0, y0, dot);
+                dot = fmaf(g1, y1, dot);
+                o4[i] = static_cast<uint32_t>(f32_to_bf16_rne(wj * g0)) |
+                        (static_cast<uint32_t>(f32_to_bf16_rne(wj * g1)) << 16);
+              }
+              buffer_store16(make_uint4(o4[0], o4[1], o4[2], o4[3]), bd, static_cast<uint32_t>(q * kWave + lane) * 16u);
+            }
           }
         } else {
           const float* go = static_cast<const float*>(d_out) + t * d;

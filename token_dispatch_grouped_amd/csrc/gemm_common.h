@@ -183,8 +183,17 @@ struct SortedTile {
   int e, mt, nt, mt_e;
 };
 
+// Row tiles of an expert are walked in groups of kRowGroup: inside a group the
+// row tile is fastest, then the column block; the last group holds the rest.
+constexpr int kRowGroup = 4;
+
 // Position p with mstart[p]*n_tiles <= tile < mstart[p+1]*n_tiles; empty experts
-// own no ids. Row tile fastest inside a column block, as in find_tile.
+// own no ids. Inside an expert, groups of kRowGroup row tiles, row tile fastest
+// inside a group: 32 consecutive ids (a round of one XCD's workgroups) cover 4
+// row tiles x 8 column blocks of a tall expert, so each weight panel crosses to
+// that XCD's L2 once per 4 row tiles and each row tile's activations once per 8
+// column blocks. An expert of at most kRowGroup row tiles is walked as by
+// find_tile.
 __device__ __forceinline__ SortedTile find_sorted_tile(const SortedTileMap& tm, int tile, int n_tiles, int e_loc) {
   int lo = 0, hi = e_loc;
   while (hi - lo > 1) {
@@ -196,7 +205,18 @@ __device__ __forceinline__ SortedTile find_sorted_tile(const SortedTileMap& tm, 
   const int ms = uniform(tm.mstart[lo]);
   const int mt_e = uniform(tm.mstart[lo + 1]) - ms;
   const int local = tile - ms * n_tiles;
-  return {uniform(tm.eid[lo]), local % mt_e, local / mt_e, mt_e};
+  const int full = mt_e / kRowGroup * kRowGroup;  // row tiles in whole groups
+  int mt, nt;
+  if (local < full * n_tiles) {
+    const int g = local / (kRowGroup * n_tiles), off = local - g * kRowGroup * n_tiles;
+    mt = g * kRowGroup + off % kRowGroup;
+    nt = off / kRowGroup;
+  } else {
+    const int rest = mt_e - full, off = local - full * n_tiles;
+    mt = full + off % rest;
+    nt = off / rest;
+  }
+  return {uniform(tm.eid[lo]), uniform(mt), uniform(nt), mt_e};
 }
 
 // Tile of round i for a workgroup whose XCD-remapped index is r: rounds go
