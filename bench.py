@@ -68,7 +68,7 @@ def stored_traffic(workload: str):
     """HBM bytes per step of the grouped GEMM from the FETCH_SIZE / WRITE_SIZE
     summary under profiles/, or None if there is none for this workload or the
     kernel sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"grouped_gemm_{workload}_traffic.md")
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
     if not os.path.exists(path):
         return None
     kv = {}
