@@ -171,6 +171,26 @@ def test_layer_all_tokens_on_one_expert():
     assert int(ref["counts"][9]) == 700
 
 
+@pytest.mark.parametrize("w", [mi.Workload("max_experts", 512, 64, 64, 1024, 8, 0, 1024, "bf16", 35),
+                               mi.Workload("k_equals_E", 200, 64, 96, 16, 16, 0, 16, "bf16", 36),
+                               mi.Workload("k_equals_E_share", 150, 96, 64, 12, 12, 4, 8, "bf16", 37)],
+                         ids=["max_experts", "k_equals_E", "k_equals_E_share"])
+def test_layer_extreme_expert_counts(w):
+    """The largest expert count the library takes (E = E_loc = 1024, so the tile
+    map holds 1024 experts, most with a row or none) and the degenerate top-k
+    with k = E, every token routed to every expert; the fused path too."""
+    res, ref = _layer_case(w)
+    logits = mi.router_logits(w)
+    x = mi.hidden_states(w)
+    wgu, wdn = mi.expert_weights(w)
+    fused = moe.layer(g.to_dev(x, w.dtype), g.to_dev(logits, "f32"), g.to_dev(wgu, w.dtype),
+                      g.to_dev(wdn, w.dtype), w.k, w.e_begin, w.e_end, fused=True)
+    torch.cuda.synchronize()
+    assert torch.equal(fused["out"].view(torch.int16), res["out"].view(torch.int16))
+    if w.k == w.E:
+        assert np.all(ref["counts"] == w.T)
+
+
 def test_layer_zero_tokens():
     w = mi.Workload("empty", 0, 64, 64, 8, 2, 0, 8, "bf16", 19)
     x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
