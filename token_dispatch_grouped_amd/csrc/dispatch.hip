@@ -7,10 +7,12 @@
 // tamanhos se combinam" (a rank owns one contiguous block of experts, so its
 // pairs are one contiguous segment of the expert-sorted pair list).
 //
-// Design (five small launches, all bounded by the pair count or HBM; a batch of
-// at most 2048 pairs takes one single-workgroup launch instead of 1-3, and one of
-// at most 65536 pairs one launch of a workgroup per 1024 pairs, each counting
-// every pair itself, then the gather):
+// Design, by the number of flat pairs P = T*k (every path gives the same
+// stable permutation; the row gather of moe_dispatch follows as one more launch):
+//   P <= 2048  : one workgroup does everything (dispatch_small_kernel);
+//   P <= 65536 : one launch, a workgroup per 1024 pairs that counts every pair
+//                itself (dispatch_onepass_kernel);
+//   larger     : four launches over per-chunk histograms in the workspace:
 //   1. count   : one workgroup per chunk of 256 (or 1024) flat pairs builds an
 //                LDS histogram and stores it expert-major: ws[e * n_chunks + c].
 //   2. scan    : two launches with one wave per expert: per-expert totals,
