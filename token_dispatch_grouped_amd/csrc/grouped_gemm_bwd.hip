@@ -99,9 +99,14 @@ __device__ __forceinline__ Operand kmajor_operand(const uint16_t* krows, int val
   return op;
 }
 
+// The bytes left are clamped at zero with a signed max (every size here is below
+// 2^31): the unsigned form becomes a saturating subtract, which has only a vector
+// instruction, and a resource held in vector registers makes the compiler wrap
+// every load that uses it in a loop over the distinct values of the wave.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t stage_rsrc(const Operand& op, int s) {
-  const uint32_t adv = static_cast<uint32_t>(s) * op.stage_step;
-  return make_rsrc(reinterpret_cast<const char*>(op.base) + adv, op.bytes > adv ? op.bytes - adv : 0u);
+  const int adv = s * static_cast<int>(op.stage_step);
+  const int left = static_cast<int>(op.bytes) - adv;
+  return make_rsrc(reinterpret_cast<const char*>(op.base) + adv, static_cast<uint32_t>(uniform(left > 0 ? left : 0)));
 }
 
 // Byte offset, inside a KROWS stage, of block-row base `rb` (a multiple of 32)
@@ -327,78 +332,76 @@ __device__ __forceinline__ void bwd_tile(uint16_t* smem, const Operand& opa, con
   // ---- epilogue: C is c_rows x c_cols (row stride ldc) at the tile origin --------
   const __amdgpu_buffer_rsrc_t rc =
       make_rsrc(C, static_cast<uint32_t>(c_rows) * static_cast<uint32_t>(ldc) * 2u);
-  // one 32 x 32 block whose rows start at row_base and whose lane column is col
-  auto store_block = [&](const f32x16_t& a, int row_base, int col) {
-    const uint32_t coff = col < c_cols ? static_cast<uint32_t>(col) * 2u : 0x80000000u;
-    if constexpr (EPI == kSwigluBwd) {
-      // a = dH at (row, f = col); G and U of the same element from gu [rows][2 N]
-      // (ldc = 2 N); dG goes to column f and dU to column N + f of C
-      const __amdgpu_buffer_rsrc_t rg = make_rsrc(gu, static_cast<uint32_t>(c_rows) * static_cast<uint32_t>(ldc) * 2u);
-      const uint32_t uoff = col < c_cols ? static_cast<uint32_t>(up_off + col) * 2u : 0x80000000u;
-      float g[16], u[16];
+  // ---- epilogue: C goes out through LDS (the stage buffers are free after the K
+  // loop), 64 rows at a time, as 16-byte vectors of 8 columns, so that a store
+  // moves two whole rows of the tile instead of one element per lane (an eighth
+  // of the store instructions, whose issue was a fifth of the TN kernel's time).
+  // The passes take wave row p / 2's blocks mi = 2 (p % 2) and the next; a
+  // 288-row NT tile's extra 32 rows, a part of which every wave holds, go in a
+  // fifth pass. Row pitch 264 floats: the two half-waves of a staging write
+  // (rows 4 apart) land in different bank halves.
+  constexpr int kPitch = 256 + 8;
+  float* stg = reinterpret_cast<float*>(smem);
+  const int tid = static_cast<int>(threadIdx.x);
+  // one 32 x 32 block into staged rows row_base.., lane column col
+  auto stage_block = [&](const f32x16_t& a, int row_base, int col) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row_base + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const uint32_t ro = static_cast<uint32_t>(row) * static_cast<uint32_t>(ldc) * 2u;
-        g[r] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rg, static_cast<int>(ro + coff), 0, 0));
-        u[r] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rg, static_cast<int>(ro + uoff), 0, 0));
-      }
+    for (int r = 0; r < 16; ++r) stg[(row_base + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * kPitch + col] = a[r];
+  };
+  auto stage_pass = [&](int p) {
+    if (wm == (p >> 1)) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row_base + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const uint32_t ro = static_cast<uint32_t>(row) * static_cast<uint32_t>(ldc) * 2u;
-        const float dh = a[r];
-        const float s = sigmoid_fast(g[r]);
-        const float dg = dh * u[r] * (s * (1.0f + g[r] * (1.0f - s)));
-        const float du = dh * g[r] * s;
-        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(dg), rc, static_cast<int>(ro + coff), 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(du), rc, static_cast<int>(ro + uoff), 0, 0);
-      }
-    } else {
+      for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row_base + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const uint32_t ro = static_cast<uint32_t>(row) * static_cast<uint32_t>(ldc) * 2u;
-        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(a[r]), rc, static_cast<int>(ro + coff), 0, 0);
-      }
+        for (int ni = 0; ni < NI; ++ni) stage_block(acc[2 * (p & 1) + m2][ni], m2 * 32, wn * 128 + blk(ni) * 32 + l31);
     }
   };
-  if constexpr (EPI == kSwigluBwd && MODE == kNT) {
-    // dH goes through LDS (the stage buffers are free after the K loop), 128 rows
-    // at a time, so that G, U, dG and dU move as 16-byte vectors of 8 columns and
-    // every thread has all its loads in flight before it waits.
-    constexpr int kPitch = 256 + 4;  // floats per staged row (16 bytes of padding against bank conflicts)
-    float* stg = reinterpret_cast<float*>(smem);
-    const int tid = static_cast<int>(threadIdx.x);
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(gu, static_cast<uint32_t>(c_rows) * static_cast<uint32_t>(ldc) * 2u);
-    // one staged block: rows row_base.. of the staging area, lane column col
-    auto stage_block = [&](const f32x16_t& a, int row_base, int col) {
+  auto stage_extra = [&] {
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        stg[(row_base + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * kPitch + col] = a[r];
-    };
-    // rows [row0, row0 + NR) of the tile, staged from row 0 of the area
-    auto finish_rows = [&](int row0, auto nr_c) {
+    for (int x = 0; x < MX; ++x) stage_block(acc_x[x], 0, wn * 128 + blk(x) * 32 + l31);
+  };
+  // 8-column chunk i of a pass: staged row rl, column col; byte offset of C row
+  // row0 + rl at column col (c_cols is a multiple of 32, so a chunk is all in
+  // range or all out; rows past c_rows fall outside the buffer and are dropped)
+  auto chunk = [&](int i, int row0, int& rl, int& col, int cshift) {
+    const int c = tid + i * kThreads;
+    rl = c >> 5;
+    col = (c & 31) * 8;
+    return col < c_cols ? static_cast<uint32_t>(row0 + rl) * static_cast<uint32_t>(ldc) * 2u +
+                              static_cast<uint32_t>(col + cshift) * 2u
+                        : 0x80000000u;
+  };
+  auto staged8 = [&](int rl, int col, float* h) {
+    const float4 h0 = *reinterpret_cast<const float4*>(stg + rl * kPitch + col);
+    const float4 h1 = *reinterpret_cast<const float4*>(stg + rl * kPitch + col + 4);
+    h[0] = h0.x, h[1] = h0.y, h[2] = h0.z, h[3] = h0.w, h[4] = h1.x, h[5] = h1.y, h[6] = h1.z, h[7] = h1.w;
+  };
+  if constexpr (EPI == kSwigluBwd && MODE == kNT) {
+    // C = [dG | dU] from the staged dH and G, U of the same elements (gu has
+    // C's layout); each pass's G and U loads go out before its rows are
+    // staged, so their latency runs under the staging
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(gu, static_cast<uint32_t>(c_rows) * static_cast<uint32_t>(ldc) * 2u);
+    auto finish_rows = [&](int row0, auto nr_c, auto&& stage_fn) {
       constexpr int NR = decltype(nr_c)::value;
       constexpr int kChunks = NR * 256 / 8 / kThreads;  // 8-column chunks per thread
-      __syncthreads();                                   // the staged rows are in LDS
       uint4 gv[kChunks], uv[kChunks];
       uint32_t go[kChunks], uo[kChunks];
 #pragma unroll
       for (int i = 0; i < kChunks; ++i) {
-        const int c = tid + i * kThreads, rl = c >> 5, col = (c & 31) * 8;
-        const uint32_t ro = static_cast<uint32_t>(row0 + rl) * static_cast<uint32_t>(ldc) * 2u;
-        go[i] = col < c_cols ? ro + static_cast<uint32_t>(col) * 2u : 0x80000000u;
-        uo[i] = col < c_cols ? ro + static_cast<uint32_t>(up_off + col) * 2u : 0x80000000u;
+        int rl, col;
+        go[i] = chunk(i, row0, rl, col, 0);
+        uo[i] = chunk(i, row0, rl, col, up_off);
         gv[i] = buffer_load16(rg, go[i]);
         uv[i] = buffer_load16(rg, uo[i]);
       }
+      stage_fn();
+      __syncthreads();  // the staged rows are in LDS
 #pragma unroll
       for (int i = 0; i < kChunks; ++i) {
-        const int c = tid + i * kThreads, rl = c >> 5, col = (c & 31) * 8;
-        const float4 h0 = *reinterpret_cast<const float4*>(stg + rl * kPitch + col);
-        const float4 h1 = *reinterpret_cast<const float4*>(stg + rl * kPitch + col + 4);
-        const float dh[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+        int rl, col;
+        chunk(i, row0, rl, col, 0);
+        float dh[8];
+        staged8(rl, col, dh);
         const uint32_t gw[4] = {gv[i].x, gv[i].y, gv[i].z, gv[i].w}, uw[4] = {uv[i].x, uv[i].y, uv[i].z, uv[i].w};
         uint32_t dgw[4], duw[4];
 #pragma unroll
@@ -419,74 +422,42 @@ __device__ __forceinline__ void bwd_tile(uint16_t* smem, const Operand& opa, con
         buffer_store16(make_uint4(dgw[0], dgw[1], dgw[2], dgw[3]), rc, go[i]);
         buffer_store16(make_uint4(duw[0], duw[1], duw[2], duw[3]), rc, uo[i]);
       }
-      __syncthreads();  // everyone has read the staged rows before the next rows are staged
+      __syncthreads();  // the staged rows are read before the next ones are written
     };
     __syncthreads();  // every wave is done with the K loop's LDS stages
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if (wm == h) {
+    for (int p = 0; p < 4; ++p) finish_rows(64 * p, std::integral_constant<int, 64>{}, [&] { stage_pass(p); });
+    if constexpr (MX > 0) finish_rows(256, std::integral_constant<int, 32>{}, stage_extra);
+  } else {
+    // plain C, rounded to bf16
+    auto write_rows = [&](int row0, auto nr_c) {
+      constexpr int NR = decltype(nr_c)::value;
+      __syncthreads();  // the staged rows are in LDS
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
+      for (int i = 0; i < NR * 256 / 8 / kThreads; ++i) {
+        int rl, col;
+        const uint32_t off = chunk(i, row0, rl, col, 0);
+        float h[8];
+        staged8(rl, col, h);
+        uint32_t w4[4];
 #pragma unroll
-          for (int mi = 0; mi < MI; ++mi) stage_block(acc[mi][ni], mi * 32, wn * 128 + blk(ni) * 32 + l31);
-      }
-      finish_rows(h * 128, std::integral_constant<int, 128>{});
-    }
-    if constexpr (MX > 0) {
-#pragma unroll
-      for (int x = 0; x < MX; ++x) stage_block(acc_x[x], 0, wn * 128 + blk(x) * 32 + l31);
-      finish_rows(256, std::integral_constant<int, 32>{});
-    }
-  } else if constexpr (MODE == kTN) {
-    // C goes out through LDS (the stage buffers are free after the K loop), 64
-    // rows at a time, as 16-byte vectors of 8 columns: a store then moves two
-    // whole rows of the tile instead of one element per lane, an eighth of the
-    // store instructions, whose issue was a fifth of this kernel's time.
-    // Row pitch 264 floats: the two half-waves of a staging write (rows 4 apart)
-    // land in different bank halves.
-    constexpr int kPitch = 256 + 8;
-    float* stg = reinterpret_cast<float*>(smem);
-    const int tid = static_cast<int>(threadIdx.x);
-    __syncthreads();  // every wave is done with the K loop's LDS stages
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {  // rows 64p ..: wave row p / 2, its blocks mi = 2 (p % 2) and the next
-      if (wm == (p >> 1)) {
-#pragma unroll
-        for (int m2 = 0; m2 < 2; ++m2)
-#pragma unroll
-          for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              stg[(m2 * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * kPitch + wn * 128 + ni * 32 + l31] =
-                  acc[2 * (p & 1) + m2][ni][r];
-      }
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < 64 * 256 / 8 / kThreads; ++i) {
-        const int c = tid + i * kThreads, rl = c >> 5, col = (c & 31) * 8;
-        const float4 h0 = *reinterpret_cast<const float4*>(stg + rl * kPitch + col);
-        const float4 h1 = *reinterpret_cast<const float4*>(stg + rl * kPitch + col + 4);
-        const uint4 v = make_uint4(
-            static_cast<uint32_t>(f32_to_bf16_rne(h0.x)) | (static_cast<uint32_t>(f32_to_bf16_rne(h0.y)) << 16),
-            static_cast<uint32_t>(f32_to_bf16_rne(h0.z)) | (static_cast<uint32_t>(f32_to_bf16_rne(h0.w)) << 16),
-            static_cast<uint32_t>(f32_to_bf16_rne(h1.x)) | (static_cast<uint32_t>(f32_to_bf16_rne(h1.y)) << 16),
-            static_cast<uint32_t>(f32_to_bf16_rne(h1.z)) | (static_cast<uint32_t>(f32_to_bf16_rne(h1.w)) << 16));
-        // c_cols is a multiple of 32: a chunk of 8 columns is all in range or all out;
-        // rows past c_rows fall outside the buffer and are dropped
-        const uint32_t off = col < c_cols ? static_cast<uint32_t>(64 * p + rl) * static_cast<uint32_t>(ldc) * 2u +
-                                                static_cast<uint32_t>(col) * 2u
-                                          : 0x80000000u;
-        buffer_store16(v, rc, off);
+        for (int q = 0; q < 4; ++q)
+          w4[q] = static_cast<uint32_t>(f32_to_bf16_rne(h[2 * q])) |
+                  (static_cast<uint32_t>(f32_to_bf16_rne(h[2 * q + 1])) << 16);
+        buffer_store16(make_uint4(w4[0], w4[1], w4[2], w4[3]), rc, off);
       }
       __syncthreads();  // the staged rows are read before the next ones are written
+    };
+    __syncthreads();  // every wave is done with the K loop's LDS stages
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      stage_pass(p);
+      write_rows(64 * p, std::integral_constant<int, 64>{});
     }
-  } else {
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) store_block(acc[mi][ni], wm * 128 + mi * 32, wn * 128 + blk(ni) * 32 + l31);
-#pragma unroll
-    for (int x = 0; x < MX; ++x) store_block(acc_x[x], 256, wn * 128 + blk(x) * 32 + l31);
+    if constexpr (MX > 0) {
+      stage_extra();
+      write_rows(256, std::integral_constant<int, 32>{});
+    }
   }
 }
 
@@ -529,6 +500,25 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_nt_kernel(
   }
 }
 
+// Tile `rem` of an expert's m_tiles x n_tiles output grid, walked in groups of
+// kRowGroup m-tiles, the m-tile fastest inside a group (the last group holds the
+// rest). 32 consecutive ids (one XCD's workgroups in a round) then cover 4
+// m-tiles x 8 n-tiles: each k-slice of an A column block crosses to that XCD's
+// L2 once per 8 tiles and each B column block once per 4 (with the n-tile
+// fastest, every tile fetched its own B block).
+__device__ __forceinline__ void grouped_mn(int rem, int m_tiles, int n_tiles, int& mt, int& nt) {
+  const int full = m_tiles / kRowGroup * kRowGroup;
+  if (rem < full * n_tiles) {
+    const int g = rem / (kRowGroup * n_tiles), off = rem - g * kRowGroup * n_tiles;
+    mt = g * kRowGroup + off % kRowGroup;
+    nt = off / kRowGroup;
+  } else {
+    const int rest = m_tiles - full, off = rem - full * n_tiles;
+    mt = full + off % rest;
+    nt = off / rest;
+  }
+}
+
 // TN: dW_e[M, N] = A_e^T @ B_e with A = src_a [rows][M], B = src_b [rows][N]
 // over each local expert's rows (K = its row count; none gives zeros).
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_tn_kernel(
@@ -543,8 +533,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_tn_kernel(
   const int base = offsets[e_begin];
   for (int tile = xcd_remap(blockIdx.x, gridDim.x); tile < total; tile += gridDim.x) {
     const int e = tile / per_e;
-    const int rem = tile - e * per_e;
-    const int mt = rem / n_tiles, nt = rem - mt * n_tiles;
+    int mt, nt;
+    grouped_mn(tile - e * per_e, m_tiles, n_tiles, mt, nt);
+    mt = uniform(mt);
+    nt = uniform(nt);
     const int r0 = uniform(min(offsets[e_begin + e] - base, n_max));
     const int rows = uniform(min(offsets[e_begin + e + 1] - base, n_max)) - r0;
     const int m0 = mt * 256, n0 = nt * 256;
