@@ -22,6 +22,13 @@
 //     row-major activations with M or N contiguous, so both are staged as
 //     [k][256] and read back transposed with ds_read_b64_tr_b16.
 // Waves: 2 x 2, each 128 x 128 (4 x 4 MFMA blocks of 32 x 32).
+//
+// [dG | dU] lives only between the launches (in the workspace), so its layout is
+// free: 32-column blocks of all N_max rows (see blk_off). A K = 32 stage of an NT
+// row tile over it is then one contiguous 16 KB run instead of 256 pieces of 64
+// bytes (on dense8 the dX product went from 1.67 to 1.45 ms that way, measured
+// with its operand addressed as blocks), and a TN stage (32 rows of a 256-column
+// slice) is eight 2 KB runs.
 #include "lds_pipe.h"
 
 namespace moe {
@@ -56,7 +63,15 @@ struct Operand {
   uint32_t stage_step;   // bytes base advances per stage
   uint32_t voff[5];      // per-lane byte offsets of this wave's loads (4, or 5 for 288 rows)
   int slot[5];           // 1 KB LDS slot of each load inside the stage
+  uint32_t voff_tail[4]; // KMAJOR over blocks: voff, or past the buffer for k-rows past the tile's
+  int tail_stage;        // last rows, in stage tail_stage (-1: none)
 };
+
+// Byte offset of element (row, col) of a [rows][cols] matrix stored in 32-column
+// blocks of n_rows rows: block col / 32 holds [n_rows][32].
+__device__ __forceinline__ uint32_t blk_off(int row, int col, int n_rows) {
+  return static_cast<uint32_t>((col >> 5) * n_rows + row) * 64u + static_cast<uint32_t>(col & 31) * 2u;
+}
 
 // KROWS operand ([row][K], K contiguous) of ROWS rows (256 or 288): load j of a
 // stage covers rows 16j..16j+15, lane L row 16j + L/4, 16-byte chunk
@@ -96,6 +111,58 @@ __device__ __forceinline__ Operand kmajor_operand(const uint16_t* krows, int val
     const int c = (lane & 31) ^ (4 * (kl & 3));
     op.voff[jj] = (static_cast<uint32_t>(kl) * static_cast<uint32_t>(ld) + static_cast<uint32_t>(col0 + 8 * c)) * 2u;
   }
+  op.tail_stage = -1;
+  return op;
+}
+
+// KROWS operand over the blocked layout: rows row0.. of a [n_rows][K] matrix in
+// 32-column blocks, so a stage is one contiguous run of its rows. Rows past the
+// tile's valid rows read whatever lies there (or zeros past the buffer): an NT
+// output row depends on its own A row only, and those output rows are not stored.
+template <int ROWS>
+__device__ __forceinline__ Operand kblk_rows_operand(const uint16_t* buf, int row0, int n_rows, int K, int wave,
+                                                     int lane) {
+  constexpr int kInstr = ROWS / 16, kPer = (kInstr + 3) / 4;
+  Operand op;
+  op.base = buf + static_cast<int64_t>(row0) * 32;
+  op.bytes = static_cast<uint32_t>(K) * static_cast<uint32_t>(n_rows) * 2u - static_cast<uint32_t>(row0) * 64u;
+  op.stage_step = static_cast<uint32_t>(n_rows) * 64u;
+#pragma unroll
+  for (int jj = 0; jj < kPer; ++jj) {
+    const int j = (wave * kPer + jj) % kInstr;
+    op.slot[jj] = j;
+    const int r = 16 * j + (lane >> 2);
+    const int c = (lane & 3) ^ ((lane >> 4) & 3);
+    op.voff[jj] = static_cast<uint32_t>(r) * 64u + static_cast<uint32_t>(c) * 16u;
+  }
+  op.tail_stage = -1;
+  return op;
+}
+
+// KMAJOR operand over the blocked layout: k-rows r0.. (valid_krows of them) of a
+// [n_rows][ld] matrix in 32-column blocks, the tile's 256 columns from col0; the
+// same LDS image as kmajor_operand. The extent of a buffer resource cannot stop
+// at the tile's last k-row here (the next rows of each block follow it), so the
+// loads of the last stage take voff_tail, which sends the lanes of k-rows past
+// valid_krows past the buffer (zeros).
+__device__ __forceinline__ Operand kblk_kmajor_operand(const uint16_t* buf, int r0, int valid_krows, int n_rows,
+                                                       int ld, int col0, int wave, int lane) {
+  Operand op;
+  op.base = buf + static_cast<int64_t>(r0) * 32;
+  op.bytes = static_cast<uint32_t>(ld) * static_cast<uint32_t>(n_rows) * 2u - static_cast<uint32_t>(r0) * 64u;
+  op.stage_step = kBK * 64u;
+  const int last = (valid_krows + kBK - 1) / kBK - 1;  // -1: no rows
+  const int rem = valid_krows - last * kBK;             // k-rows of the last stage
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int j = wave * 4 + jj;
+    op.slot[jj] = j;
+    const int kl = 2 * j + (lane >> 5);
+    const int c = (lane & 31) ^ (4 * (kl & 3));
+    op.voff[jj] = blk_off(kl, col0 + 8 * c, n_rows);
+    op.voff_tail[jj] = kl < rem ? op.voff[jj] : 0x80000000u;
+  }
+  op.tail_stage = rem < kBK ? last : -1;
   return op;
 }
 
@@ -138,10 +205,15 @@ __device__ __forceinline__ void mfma_vgpr(f32x16_t& c, const bf16x8_t& a, const 
 // wave multiplies them by two of its four column blocks. The second wave row keeps
 // its column blocks in swapped slots (block = slot ^ 2), so that both wave rows use
 // slots 0 and 1 for the extra rows and together cover all four blocks.
-template <int MODE, int EPI, int XR>
+// BBLK (TN): B is a blocked KMAJOR operand (kblk_kmajor_operand), whose last
+// stage takes its tail offsets. CBLK (NT with kSwigluBwd): C is the blocked
+// [dG | dU] of cblk_rows rows, C pointing at its start and (crow0, ccol0) the
+// tile's origin in it; otherwise C points at the tile's origin, row stride ldc.
+template <int MODE, int EPI, int XR, bool BBLK = false, bool CBLK = false>
 __device__ __forceinline__ void bwd_tile(uint16_t* smem, const Operand& opa, const Operand& opb, int ksteps,
                                          uint16_t* __restrict__ C, int c_rows, int c_cols, int ldc,
-                                         const uint16_t* __restrict__ gu, int up_off) {
+                                         const uint16_t* __restrict__ gu, int up_off, int cblk_rows = 0,
+                                         int crow0 = 0, int ccol0 = 0) {
   static_assert(XR == 0 || MODE == kNT, "extra rows only in NT tiles");
   constexpr int MX = XR ? 2 : 0;                                     // extra MFMA blocks per wave
   constexpr int NA = XR ? 5 : 4;                                     // activation loads per wave per stage
@@ -245,15 +317,22 @@ __device__ __forceinline__ void bwd_tile(uint16_t* smem, const Operand& opa, con
   struct StageLoads {
     __amdgpu_buffer_rsrc_t ra, rb;
     uint32_t la, lb;
+    bool tail_b;  // BBLK: B's loads take their tail offsets
   };
   auto stage_loads = [&](int s) {
     const int buf = s % kStages;
-    return StageLoads{stage_rsrc(opa, s), stage_rsrc(opb, s), sA + buf * kAStage, sB + buf * kOpStageBytes};
+    return StageLoads{stage_rsrc(opa, s), stage_rsrc(opb, s), sA + buf * kAStage, sB + buf * kOpStageBytes,
+                      BBLK && s == opb.tail_stage};
   };
   auto dma_one = [&](const StageLoads& st, auto j_c) {
     constexpr int j = decltype(j_c)::value;
-    if constexpr (j < NA) dma16(st.ra, opa.voff[j], st.la + opa.slot[j] * 1024);
-    else dma16(st.rb, opb.voff[j - NA], st.lb + opb.slot[j - NA] * 1024);
+    if constexpr (j < NA) {
+      dma16(st.ra, opa.voff[j], st.la + opa.slot[j] * 1024);
+    } else if constexpr (BBLK) {
+      dma16(st.rb, st.tail_b ? opb.voff_tail[j - NA] : opb.voff[j - NA], st.lb + opb.slot[j - NA] * 1024);
+    } else {
+      dma16(st.rb, opb.voff[j - NA], st.lb + opb.slot[j - NA] * 1024);
+    }
   };
   auto wait_stage = [&](int s) {
     const int after = min(kStages - 2, ksteps - 1 - s);
@@ -331,7 +410,8 @@ __device__ __forceinline__ void bwd_tile(uint16_t* smem, const Operand& opa, con
 
   // ---- epilogue: C is c_rows x c_cols (row stride ldc) at the tile origin --------
   const __amdgpu_buffer_rsrc_t rc =
-      make_rsrc(C, static_cast<uint32_t>(c_rows) * static_cast<uint32_t>(ldc) * 2u);
+      CBLK ? make_rsrc(C, static_cast<uint32_t>(cblk_rows) * static_cast<uint32_t>(ldc) * 2u)
+           : make_rsrc(C, static_cast<uint32_t>(c_rows) * static_cast<uint32_t>(ldc) * 2u);
   // ---- epilogue: C goes out through LDS (the stage buffers are free after the K
   // loop), 64 rows at a time, as 16-byte vectors of 8 columns, so that a store
   // moves two whole rows of the tile instead of one element per lane (an eighth
@@ -371,6 +451,19 @@ __device__ __forceinline__ void bwd_tile(uint16_t* smem, const Operand& opa, con
                               static_cast<uint32_t>(col + cshift) * 2u
                         : 0x80000000u;
   };
+  // byte offset in C of tile row row0 + rl, tile column col + cshift (past the
+  // buffer for rows past c_rows and columns past c_cols): the blocked [dG | dU]
+  // with CBLK (ldc = its column count), else row-major from the tile's origin
+  auto cstore = [&](int rl, int row0, int col, int cshift) -> uint32_t {
+    if constexpr (CBLK) {
+      return row0 + rl < c_rows && col < c_cols ? blk_off(crow0 + row0 + rl, ccol0 + col + cshift, cblk_rows)
+                                                : 0x80000000u;
+    } else {
+      return col < c_cols ? static_cast<uint32_t>(row0 + rl) * static_cast<uint32_t>(ldc) * 2u +
+                                static_cast<uint32_t>(col + cshift) * 2u
+                          : 0x80000000u;
+    }
+  };
   auto staged8 = [&](int rl, int col, float* h) {
     const float4 h0 = *reinterpret_cast<const float4*>(stg + rl * kPitch + col);
     const float4 h1 = *reinterpret_cast<const float4*>(stg + rl * kPitch + col + 4);
@@ -385,14 +478,11 @@ __device__ __forceinline__ void bwd_tile(uint16_t* smem, const Operand& opa, con
       constexpr int NR = decltype(nr_c)::value;
       constexpr int kChunks = NR * 256 / 8 / kThreads;  // 8-column chunks per thread
       uint4 gv[kChunks], uv[kChunks];
-      uint32_t go[kChunks], uo[kChunks];
 #pragma unroll
       for (int i = 0; i < kChunks; ++i) {
         int rl, col;
-        go[i] = chunk(i, row0, rl, col, 0);
-        uo[i] = chunk(i, row0, rl, col, up_off);
-        gv[i] = buffer_load16(rg, go[i]);
-        uv[i] = buffer_load16(rg, uo[i]);
+        gv[i] = buffer_load16(rg, chunk(i, row0, rl, col, 0));
+        uv[i] = buffer_load16(rg, chunk(i, row0, rl, col, up_off));
       }
       stage_fn();
       __syncthreads();  // the staged rows are in LDS
@@ -419,8 +509,8 @@ __device__ __forceinline__ void bwd_tile(uint16_t* smem, const Operand& opa, con
           dgw[q] = dgp;
           duw[q] = dup;
         }
-        buffer_store16(make_uint4(dgw[0], dgw[1], dgw[2], dgw[3]), rc, go[i]);
-        buffer_store16(make_uint4(duw[0], duw[1], duw[2], duw[3]), rc, uo[i]);
+        buffer_store16(make_uint4(dgw[0], dgw[1], dgw[2], dgw[3]), rc, cstore(rl, row0, col, 0));
+        buffer_store16(make_uint4(duw[0], duw[1], duw[2], duw[3]), rc, cstore(rl, row0, col, up_off));
       }
       __syncthreads();  // the staged rows are read before the next ones are written
     };
@@ -462,8 +552,10 @@ __device__ __forceinline__ void bwd_tile(uint16_t* smem, const Operand& opa, con
 }
 
 // NT: C[rows, N] = A[rows, K] @ B_e[N, K]^T over row tiles of each local expert.
-// EPI = kSwigluBwd: A = dY, B = W_dn (N = d_ff, K = d), C = [dG | dU] with row
-// stride 2 N, gu = [G | U] of the same rows.
+// EPI = kSwigluBwd: A = dY, B = W_dn (N = d_ff, K = d), gu = [G | U] of the same
+// rows (row stride ldc = 2 N), C = [dG | dU] in the blocked layout (blk_off, n_max
+// rows, ldc columns). EPI = kPlain: A = that blocked [dG | dU] (K = 2 d_ff),
+// B = W_gu, C = dX row-major (row stride ldc).
 template <int EPI>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_nt_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
@@ -487,14 +579,24 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_nt_kernel(
     const int n0 = tc.nt * 256;
     const uint16_t* Bexp = B + static_cast<int64_t>(tc.e) * N * K;
     const Operand opb = krows_operand<256>(Bexp + static_cast<int64_t>(n0) * K, N - n0, K, wave, lane);
-    uint16_t* Ct = C + static_cast<int64_t>(row0) * ldc + n0;
-    const uint16_t* gut = EPI == kSwigluBwd ? gu + static_cast<int64_t>(row0) * ldc + n0 : nullptr;
-    if (rows > 256) {
-      const Operand opa = krows_operand<288>(A + static_cast<int64_t>(row0) * K, rows, K, wave, lane);
-      bwd_tile<kNT, EPI, 1>(smem, opa, opb, K / kBK, Ct, rows, N - n0, ldc, gut, N);
+    if constexpr (EPI == kSwigluBwd) {
+      const uint16_t* gut = gu + static_cast<int64_t>(row0) * ldc + n0;
+      if (rows > 256) {
+        const Operand opa = krows_operand<288>(A + static_cast<int64_t>(row0) * K, rows, K, wave, lane);
+        bwd_tile<kNT, EPI, 1, false, true>(smem, opa, opb, K / kBK, C, rows, N - n0, ldc, gut, N, n_max, row0, n0);
+      } else {
+        const Operand opa = krows_operand<256>(A + static_cast<int64_t>(row0) * K, rows, K, wave, lane);
+        bwd_tile<kNT, EPI, 0, false, true>(smem, opa, opb, K / kBK, C, rows, N - n0, ldc, gut, N, n_max, row0, n0);
+      }
     } else {
-      const Operand opa = krows_operand<256>(A + static_cast<int64_t>(row0) * K, rows, K, wave, lane);
-      bwd_tile<kNT, EPI, 0>(smem, opa, opb, K / kBK, Ct, rows, N - n0, ldc, gut, N);
+      uint16_t* Ct = C + static_cast<int64_t>(row0) * ldc + n0;
+      if (rows > 256) {
+        const Operand opa = kblk_rows_operand<288>(A, row0, n_max, K, wave, lane);
+        bwd_tile<kNT, EPI, 1>(smem, opa, opb, K / kBK, Ct, rows, N - n0, ldc, nullptr, 0);
+      } else {
+        const Operand opa = kblk_rows_operand<256>(A, row0, n_max, K, wave, lane);
+        bwd_tile<kNT, EPI, 0>(smem, opa, opb, K / kBK, Ct, rows, N - n0, ldc, nullptr, 0);
+      }
     }
     __builtin_amdgcn_s_barrier();
   }
@@ -520,7 +622,9 @@ __device__ __forceinline__ void grouped_mn(int rem, int m_tiles, int n_tiles, in
 }
 
 // TN: dW_e[M, N] = A_e^T @ B_e with A = src_a [rows][M], B = src_b [rows][N]
-// over each local expert's rows (K = its row count; none gives zeros).
+// over each local expert's rows (K = its row count; none gives zeros). BBLK: B is
+// the blocked [dG | dU] (blk_off, n_max rows).
+template <bool BBLK>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_tn_kernel(
     const uint16_t* __restrict__ src_a, const uint16_t* __restrict__ src_b, uint16_t* __restrict__ dW,
     const int32_t* __restrict__ offsets, int e_begin, int e_loc, int M, int N, int n_max) {
@@ -541,8 +645,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_tn_kernel(
     const int rows = uniform(min(offsets[e_begin + e + 1] - base, n_max)) - r0;
     const int m0 = mt * 256, n0 = nt * 256;
     const Operand opa = kmajor_operand(src_a + static_cast<int64_t>(r0) * M, rows, M, m0, wave, lane);
-    const Operand opb = kmajor_operand(src_b + static_cast<int64_t>(r0) * N, rows, N, n0, wave, lane);
-    bwd_tile<kTN, kPlain, 0>(smem, opa, opb, (rows + kBK - 1) / kBK,
+    const Operand opb = BBLK ? kblk_kmajor_operand(src_b, r0, rows, n_max, N, n0, wave, lane)
+                             : kmajor_operand(src_b + static_cast<int64_t>(r0) * N, rows, N, n0, wave, lane);
+    bwd_tile<kTN, kPlain, 0, BBLK>(smem, opa, opb, (rows + kBK - 1) / kBK,
                           dW + static_cast<int64_t>(e) * M * N + static_cast<int64_t>(m0) * N + n0, M - m0, N - n0, N,
                           nullptr, 0);
     __builtin_amdgcn_s_barrier();
@@ -567,10 +672,16 @@ hipError_t launch_grouped_gemm_nt(const void* a, const void* b, void* c, const v
 }
 
 hipError_t launch_grouped_gemm_tn(const void* src_a, const void* src_b, void* dw, const int32_t* offsets,
-                                  int e_begin, int e_loc, int M, int N, int64_t n_max, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(grouped_gemm_tn_kernel, dim3(grid), dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t*>(src_a), static_cast<const uint16_t*>(src_b),
-                     static_cast<uint16_t*>(dw), offsets, e_begin, e_loc, M, N, static_cast<int>(n_max));
+                                  int e_begin, int e_loc, int M, int N, int64_t n_max, bool b_blocked, int grid,
+                                  hipStream_t stream) {
+  if (b_blocked)
+    hipLaunchKernelGGL(grouped_gemm_tn_kernel<true>, dim3(grid), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(src_a), static_cast<const uint16_t*>(src_b),
+                       static_cast<uint16_t*>(dw), offsets, e_begin, e_loc, M, N, static_cast<int>(n_max));
+  else
+    hipLaunchKernelGGL(grouped_gemm_tn_kernel<false>, dim3(grid), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(src_a), static_cast<const uint16_t*>(src_b),
+                       static_cast<uint16_t*>(dw), offsets, e_begin, e_loc, M, N, static_cast<int>(n_max));
   return hipGetLastError();
 }
 

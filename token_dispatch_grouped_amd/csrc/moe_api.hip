@@ -285,7 +285,8 @@ moe_status gemm_backward(const moe_shape* s, moe_dtype dt, const void* x, const 
       e = moe::launch_grouped_gemm_plain(x_perm, w_gate_up, ws + off_gu, offsets, s->e_begin, e_loc, d, 2 * d_ff,
                                          2 * d_ff, n_max,
                                          moe::grouped_gemm_grid(n_max, e_loc, (2 * d_ff + 255) / 256), stream);
-    // [dG | dU] from dH = dY @ W_dn^T and [G | U]
+    // [dG | dU] from dH = dY @ W_dn^T and [G | U], written in 32-column blocks of N_max rows (the
+    // layout the next two products read fastest)
     if (e == hipSuccess)
       e = moe::launch_grouped_gemm_nt(d_y, w_down, d_gu, gu, offsets, s->e_begin, e_loc, d, d_ff, 2 * d_ff, n_max,
                                       true, moe::grouped_gemm_grid(n_max, e_loc, (d_ff + 255) / 256), stream);
@@ -303,10 +304,10 @@ moe_status gemm_backward(const moe_shape* s, moe_dtype dt, const void* x, const 
     return static_cast<int>(g < 1 ? 1 : g);
   };
   if (e == hipSuccess)
-    e = moe::launch_grouped_gemm_tn(h, d_y, d_w_down, offsets, s->e_begin, e_loc, d_ff, d, n_max, tn_grid(d_ff, d),
-                                    stream);
+    e = moe::launch_grouped_gemm_tn(h, d_y, d_w_down, offsets, s->e_begin, e_loc, d_ff, d, n_max, false,
+                                    tn_grid(d_ff, d), stream);
   if (e == hipSuccess)
-    e = moe::launch_grouped_gemm_tn(x_perm, d_gu, d_w_gate_up, offsets, s->e_begin, e_loc, d, 2 * d_ff, n_max,
+    e = moe::launch_grouped_gemm_tn(x_perm, d_gu, d_w_gate_up, offsets, s->e_begin, e_loc, d, 2 * d_ff, n_max, true,
                                     tn_grid(d, 2 * d_ff), stream);
   return from_hip(e);
 }
