@@ -137,6 +137,42 @@ def test_backward_rejects_unsupported_shapes():
     assert e.value.status == moe.MOE_EUNSUPPORTED
 
 
+@pytest.mark.parametrize("w", [CASES[1], CASES[2]], ids=[CASES[1].name, CASES[2].name])
+def test_backward_ignores_workspace_contents(w):
+    """The workspace's rows past N_loc are never written; the gradients must not
+    read them. Filled with NaN (0xFFFF) or with zeros before the call, both
+    backward entry points give the same bits (the last expert's row count is not a
+    multiple of 32 here, so the weight gradients' last K stage ends inside a block
+    of the workspace's [dG | dU])."""
+    logits = mi.router_logits(w)
+    x = mi.hidden_states(w)
+    wgu, wdn = mi.expert_weights(w)
+    print(f"case {w}", flush=True)
+    dx, dl = g.to_dev(x, "bf16"), g.to_dev(logits, "f32")
+    dgu, ddn = g.to_dev(wgu, "bf16"), g.to_dev(wdn, "bf16")
+    fwd = moe.layer(dx, dl, dgu, ddn, w.k, w.e_begin, w.e_end, fused=True, save=True)
+    offs = fwd["offsets"].cpu().numpy()
+    n_loc = int(offs[w.e_end] - offs[w.e_begin])
+    n_max = w.T * min(w.k, w.E_loc)
+    last = [int(c) for c in np.diff(offs)[w.e_begin:w.e_end] if c > 0][-1]
+    assert n_loc < n_max and last % 32 != 0, (n_loc, n_max, last)
+    rng = np.random.default_rng(w.seed + 900)
+    d_y = g.to_dev(mi.f32_to_bf16_bits(rng.standard_normal((n_max, w.d)).astype(np.float32)), "bf16")
+    ws_bytes = moe.grouped_gemm_backward_workspace_bytes(w.T, w.d, w.d_ff, w.E, w.k, w.e_begin, w.e_end)
+    for gu in (None, fwd["gu"]):
+        outs = []
+        for fill in (0xFF, 0x00):
+            ws = torch.full((ws_bytes,), fill, dtype=torch.uint8, device="cuda")
+            outs.append(moe.grouped_gemm_backward(dx, fwd["perm"], fwd["offsets"], dgu, ddn, fwd["h"], d_y, w.k, w.E,
+                                                  w.e_begin, w.e_end, workspace=ws, gu=gu))
+        torch.cuda.synchronize()
+        (dxp0, dgu0, ddn0), (dxp1, dgu1, ddn1) = outs
+        assert torch.equal(dxp0[:n_loc].view(torch.int16), dxp1[:n_loc].view(torch.int16))
+        assert torch.equal(dgu0.view(torch.int16), dgu1.view(torch.int16))
+        assert torch.equal(ddn0.view(torch.int16), ddn1.view(torch.int16))
+        assert not torch.isnan(dgu0.float()).any()
+
+
 # ----------------------------------------------------------------------------- kept pre-activations
 
 def _split_counts(counts):

@@ -105,6 +105,7 @@ struct SortedTileMap {
   int eid[kMaxExperts];         // local expert at each position
   int rstart[kMaxExperts + 1];  // first row of each expert (by expert id), relative to the local segment
   int classes;                  // height classes that hold at least one expert with rows
+  int tall;                     // positions [0, tall) hold the class-0 experts
 };
 
 __device__ __forceinline__ int height_class(int rows) {
@@ -133,6 +134,7 @@ __device__ void build_sorted_tile_map(SortedTileMap& tm, const int32_t* __restri
     if (lane == 0) {
       tm.rstart[e_loc] = min(offsets[e_begin + e_loc] - base, n_max);
       tm.classes = (cnt[0] > 0) + (cnt[1] > 0) + (cnt[2] > 0) + (cnt[3] > 0);
+      tm.tall = cnt[0];
     }
     int cbase[5];
     cbase[0] = 0;

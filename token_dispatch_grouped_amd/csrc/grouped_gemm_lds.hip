@@ -542,23 +542,32 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_lds_kernel(
   // Balance: when the last round would keep at most half of the workgroups busy
   // and every expert's tiles have the same height class (so that the rounds
   // before it end together), its tiles are split into half-width tiles, two per
-  // tile, and that round takes a little over half as long. (With mixed classes
-  // the workgroups that would take the halves include ones whose earlier tiles
-  // were the costly ones.) A last column block with at most half of its columns
-  // in range is computed as a half-width tile when it has more than 32 rows (a
-  // 32-row tile streams weights, and measured no faster at half width).
+  // tile, and that round takes a little over half as long. With several classes
+  // the tiles come tallest class first, so every workgroup's earlier rounds were
+  // full-height tiles; there only the last round's tiles of class-0 experts are
+  // split, when their halves and the round's other (lighter) tiles still fit in
+  // one round (skew256's gate/up: 16 full tiles past four rounds became 32 half
+  // tiles beside the 144 light ones). A last column block with at most half of
+  // its columns in range is computed as a half-width tile when it has more than
+  // 32 rows (a 32-row tile streams weights, and measured no faster at half width).
   const int G = gridDim.x, r = xcd_remap(blockIdx.x, G);
   const int rounds = (total + G - 1) / G;
   const int last = total - (rounds - 1) * G;
-  const bool split = total > 0 && 2 * last <= G && uniform(tm.classes) == 1;
+  const int tall_last = min(max(uniform(tm.mstart[uniform(tm.tall)]) * n_tiles - (rounds - 1) * G, 0), last);
+  const int n_split = uniform(tm.classes) == 1 ? last : tall_last;  // last-round tiles split in two
+  const bool split = total > 0 && n_split > 0 && last + n_split <= G;
   const bool narrow_last = N - (n_tiles - 1) * kOutCols <= kOutCols / 2;
   for (int i = 0;; ++i) {
     int tile, part = 0;  // part: 0 the whole tile, 1 or 2 its first or second half
     if (split && i == rounds - 1) {
-      const int h = (i & 1) ? G - 1 - r : r;  // half tiles in the snake's direction
-      if (h >= 2 * last) break;
-      tile = (rounds - 1) * G + (h >> 1);
-      part = 1 + (h & 1);
+      const int h = (i & 1) ? G - 1 - r : r;  // items of the round in the snake's direction
+      if (h < 2 * n_split) {
+        tile = (rounds - 1) * G + (h >> 1);
+        part = 1 + (h & 1);
+      } else {
+        tile = (rounds - 1) * G + n_split + (h - 2 * n_split);
+        if (tile >= total) break;
+      }
     } else {
       tile = snake_tile(i, r, G);
       if (tile >= total) break;  // later rounds hold only larger ids
