@@ -239,8 +239,8 @@ moe_status moe_combine_backward(const moe_shape* s, moe_dtype dt, const void* d_
                                 void* d_y, float* d_topk_w, hipStream_t stream);
 
 /* Bytes of device workspace moe_grouped_gemm_backward needs (0 unless dt is
- * MOE_BF16): the gathered rows, and the gate/up pre-activations and their
- * gradient, each for N_max rows. */
+ * MOE_BF16): the gathered rows, a copy of d_y, and the gate/up pre-activations
+ * and their gradient, each for N_max rows. */
 size_t moe_grouped_gemm_backward_workspace_bytes(const moe_shape* s, moe_dtype dt);
 
 /* Gradient of the grouped expert FFN (moe_grouped_gemm / _gather). For each local

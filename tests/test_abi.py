@@ -189,11 +189,12 @@ def test_backward_entry_points_validate_on_the_host():
         p = [FAKE] * 4
         p[i] = NULL
         assert lib.moe_route_topk_backward(ctypes.byref(s), *p, NULL) == moe.MOE_EINVAL, i
-    # workspace: x_perm [N_max, d] and two [N_max, 2 d_ff] blocks, each 256-byte aligned; none for fp32
+    # workspace: x_perm [N_max, d], two [N_max, 2 d_ff] blocks and a blocked copy of d_y [N_max, d], each
+    # 256-byte aligned; none for fp32
     s = _shape(T=16, d=64, d_ff=64, k=2)
     n_max = 32
     assert lib.moe_grouped_gemm_backward_workspace_bytes(ctypes.byref(s), moe.MOE_BF16) == \
-        n_max * 64 * 2 + 2 * n_max * 128 * 2
+        2 * n_max * 64 * 2 + 2 * n_max * 128 * 2
     assert lib.moe_grouped_gemm_backward_workspace_bytes(ctypes.byref(s), moe.MOE_F32) == 0
 
 

@@ -23,12 +23,13 @@
 //     [k][256] and read back transposed with ds_read_b64_tr_b16.
 // Waves: 2 x 2, each 128 x 128 (4 x 4 MFMA blocks of 32 x 32).
 //
-// [dG | dU] lives only between the launches (in the workspace), so its layout is
-// free: 32-column blocks of all N_max rows (see blk_off). A K = 32 stage of an NT
-// row tile over it is then one contiguous 16 KB run instead of 256 pieces of 64
-// bytes (on dense8 the dX product went from 1.67 to 1.45 ms that way, measured
-// with its operand addressed as blocks), and a TN stage (32 rows of a 256-column
-// slice) is eight 2 KB runs.
+// The A operands of both NT products live in the workspace in 32-column blocks
+// of all N_max rows (see blk_off): [dG | dU], which exists only between the
+// launches, and a copy of dY made for the purpose. A K = 32 stage of an NT row
+// tile is then one contiguous 16 KB run instead of 256 pieces of 64 bytes (on
+// dense8, dX went from 1.70 to 1.50 ms and dH from 1.01 to 0.90 with their
+// operands addressed as blocks); a TN stage over [dG | dU] (32 rows of a
+// 256-column slice) is eight 2 KB runs.
 #include "lds_pipe.h"
 
 namespace moe {
@@ -551,11 +552,12 @@ __device__ __forceinline__ void bwd_tile(uint16_t* smem, const Operand& opa, con
   }
 }
 
-// NT: C[rows, N] = A[rows, K] @ B_e[N, K]^T over row tiles of each local expert.
+// NT: C[rows, N] = A[rows, K] @ B_e[N, K]^T over row tiles of each local expert,
+// A in the blocked layout (blk_off, n_max rows, K columns).
 // EPI = kSwigluBwd: A = dY, B = W_dn (N = d_ff, K = d), gu = [G | U] of the same
-// rows (row stride ldc = 2 N), C = [dG | dU] in the blocked layout (blk_off, n_max
-// rows, ldc columns). EPI = kPlain: A = that blocked [dG | dU] (K = 2 d_ff),
-// B = W_gu, C = dX row-major (row stride ldc).
+// rows (row stride ldc = 2 N), C = [dG | dU], blocked (n_max rows, ldc columns).
+// EPI = kPlain: A = that [dG | dU] (K = 2 d_ff), B = W_gu, C = dX row-major (row
+// stride ldc).
 template <int EPI>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_nt_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
@@ -582,10 +584,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_nt_kernel(
     if constexpr (EPI == kSwigluBwd) {
       const uint16_t* gut = gu + static_cast<int64_t>(row0) * ldc + n0;
       if (rows > 256) {
-        const Operand opa = krows_operand<288>(A + static_cast<int64_t>(row0) * K, rows, K, wave, lane);
+        const Operand opa = kblk_rows_operand<288>(A, row0, n_max, K, wave, lane);
         bwd_tile<kNT, EPI, 1, false, true>(smem, opa, opb, K / kBK, C, rows, N - n0, ldc, gut, N, n_max, row0, n0);
       } else {
-        const Operand opa = krows_operand<256>(A + static_cast<int64_t>(row0) * K, rows, K, wave, lane);
+        const Operand opa = kblk_rows_operand<256>(A, row0, n_max, K, wave, lane);
         bwd_tile<kNT, EPI, 0, false, true>(smem, opa, opb, K / kBK, C, rows, N - n0, ldc, gut, N, n_max, row0, n0);
       }
     } else {
@@ -654,7 +656,41 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_tn_kernel(
   }
 }
 
+// Rows [0, N_loc) of a row-major [N_max][cols] matrix into the blocked layout
+// (blk_off, n_max rows): one 16-byte chunk of 8 columns per thread. Eight
+// consecutive threads take rows 2m and 2m + 1 of one 32-column block (one
+// 128-byte line of the destination), the next eight the next block: a wave reads
+// two whole 512-byte row pieces and writes eight whole lines.
+__global__ __launch_bounds__(kThreads) void to_blocked_kernel(const uint4* __restrict__ src, uint16_t* __restrict__ dst,
+                                                             const int32_t* __restrict__ offsets, int e_begin,
+                                                             int e_end, int cols, int n_max) {
+  const int n_loc = min(offsets[e_end] - offsets[e_begin], n_max);
+  const int nb = cols / 32;
+  const int64_t items = static_cast<int64_t>((n_loc + 1) / 2) * nb * 8;
+  for (int64_t it = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; it < items;
+       it += static_cast<int64_t>(gridDim.x) * kThreads) {
+    const int sub = static_cast<int>(it & 3), rp = static_cast<int>((it >> 2) & 1);
+    const int64_t rest = it >> 3;
+    const int m = static_cast<int>(rest / nb), b = static_cast<int>(rest - static_cast<int64_t>(m) * nb);
+    const int r = 2 * m + rp;
+    if (r < n_loc)
+      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(dst) + blk_off(r, b * 32 + sub * 8, n_max)) =
+          src[static_cast<int64_t>(r) * (cols / 8) + b * 4 + sub];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_to_blocked(const void* src, void* dst, const int32_t* offsets, int e_begin, int e_end, int cols,
+                             int64_t n_max, hipStream_t stream) {
+  int64_t blocks = (n_max * (cols / 8) + kThreads - 1) / kThreads;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(to_blocked_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
+                     static_cast<const uint4*>(src), static_cast<uint16_t*>(dst), offsets, e_begin, e_end, cols,
+                     static_cast<int>(n_max));
+  return hipGetLastError();
+}
 
 hipError_t launch_grouped_gemm_nt(const void* a, const void* b, void* c, const void* gu, const int32_t* offsets,
                                   int e_begin, int e_loc, int K, int N, int ldc, int64_t n_max, bool swiglu_bwd,

@@ -36,14 +36,16 @@ int64_t n_max_of(const moe_shape* s) {
 
 constexpr size_t kWsAlign = 256;
 size_t align_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
-// workspace of moe_grouped_gemm_backward: x_perm [N_max, d], gu and d_gu [N_max, 2 d_ff]
-size_t backward_ws(const moe_shape* s, size_t* off_gu, size_t* off_dgu) {
+// workspace of moe_grouped_gemm_backward: x_perm [N_max, d], gu and d_gu [N_max, 2 d_ff], and dY in
+// 32-column blocks [N_max, d]
+size_t backward_ws(const moe_shape* s, size_t* off_gu, size_t* off_dgu, size_t* off_dyb = nullptr) {
   const size_t n = static_cast<size_t>(n_max_of(s));
   const size_t xp = align_up(n * static_cast<size_t>(s->d) * 2);
   const size_t g = align_up(n * static_cast<size_t>(s->d_ff) * 2 * 2);
   if (off_gu) *off_gu = xp;
   if (off_dgu) *off_dgu = xp + g;
-  return xp + 2 * g;
+  if (off_dyb) *off_dyb = xp + 2 * g;
+  return 2 * xp + 2 * g;
 }
 
 }  // namespace
@@ -270,12 +272,13 @@ moe_status gemm_backward(const moe_shape* s, moe_dtype dt, const void* x, const 
     return MOE_EUNSUPPORTED;
   const int e_loc = s->e_end - s->e_begin;
   const int d = s->d, d_ff = s->d_ff;
-  size_t off_gu = 0, off_dgu = 0;
-  backward_ws(s, &off_gu, &off_dgu);
+  size_t off_gu = 0, off_dgu = 0, off_dyb = 0;
+  backward_ws(s, &off_gu, &off_dgu, &off_dyb);
   char* ws = static_cast<char*>(workspace);
   void* x_perm = ws;
   const void* gu = saved != nullptr ? saved : static_cast<const void*>(ws + off_gu);
   void* d_gu = ws + off_dgu;
+  void* d_y_blk = ws + off_dyb;
   hipError_t e = hipSuccess;
   if (n_max > 0) {
     // the rows of the local pairs, then (unless the forward kept them) their gate/up pre-activations
@@ -285,11 +288,12 @@ moe_status gemm_backward(const moe_shape* s, moe_dtype dt, const void* x, const 
       e = moe::launch_grouped_gemm_plain(x_perm, w_gate_up, ws + off_gu, offsets, s->e_begin, e_loc, d, 2 * d_ff,
                                          2 * d_ff, n_max,
                                          moe::grouped_gemm_grid(n_max, e_loc, (2 * d_ff + 255) / 256), stream);
-    // [dG | dU] from dH = dY @ W_dn^T and [G | U], written in 32-column blocks of N_max rows (the
-    // layout the next two products read fastest)
+    // [dG | dU] from dH = dY @ W_dn^T and [G | U]; dY read, and [dG | dU] written, in 32-column
+    // blocks of N_max rows (the layout the products read fastest)
+    if (e == hipSuccess) e = moe::launch_to_blocked(d_y, d_y_blk, offsets, s->e_begin, s->e_end, d, n_max, stream);
     if (e == hipSuccess)
-      e = moe::launch_grouped_gemm_nt(d_y, w_down, d_gu, gu, offsets, s->e_begin, e_loc, d, d_ff, 2 * d_ff, n_max,
-                                      true, moe::grouped_gemm_grid(n_max, e_loc, (d_ff + 255) / 256), stream);
+      e = moe::launch_grouped_gemm_nt(d_y_blk, w_down, d_gu, gu, offsets, s->e_begin, e_loc, d, d_ff, 2 * d_ff,
+                                      n_max, true, moe::grouped_gemm_grid(n_max, e_loc, (d_ff + 255) / 256), stream);
     // dX_perm = [dG | dU] @ W_gu^T
     if (e == hipSuccess)
       e = moe::launch_grouped_gemm_nt(d_gu, w_gate_up, d_x_perm, nullptr, offsets, s->e_begin, e_loc, 2 * d_ff, d,

@@ -93,12 +93,15 @@ hipError_t launch_gather_rows(const void* x, size_t row_bytes, const int32_t* pe
 // C[rows, N] = A[rows, K] @ B_e[K, N] (N-contiguous weights, row stride ldb) per local expert
 hipError_t launch_grouped_gemm_plain(const void* a, const void* b, void* c, const int32_t* offsets, int e_begin,
                                      int e_loc, int K, int N, int ldb, int64_t n_max, int grid, hipStream_t stream);
-// C[rows, N] = A[rows, K] @ B_e[N, K]^T (K-contiguous weights). With swiglu_bwd, A = dY, B = W_dn and C
-// receives [dG | dU] in 32-column blocks of n_max rows from the [G | U] rows in gu (row stride ldc = 2 N);
-// without, A is that blocked [dG | dU] (K = 2 d_ff) and C is row-major (row stride ldc)
+// C[rows, N] = A[rows, K] @ B_e[N, K]^T (K-contiguous weights), A in 32-column blocks of n_max rows. With
+// swiglu_bwd, A = dY, B = W_dn and C receives [dG | dU], blocked the same way, from the [G | U] rows in gu (row
+// stride ldc = 2 N); without, A is that [dG | dU] (K = 2 d_ff) and C is row-major (row stride ldc)
 hipError_t launch_grouped_gemm_nt(const void* a, const void* b, void* c, const void* gu, const int32_t* offsets,
                                   int e_begin, int e_loc, int K, int N, int ldc, int64_t n_max, bool swiglu_bwd,
                                   int grid, hipStream_t stream);
+// rows [0, N_loc) of the row-major [n_max][cols] src into dst in 32-column blocks of n_max rows
+hipError_t launch_to_blocked(const void* src, void* dst, const int32_t* offsets, int e_begin, int e_end, int cols,
+                             int64_t n_max, hipStream_t stream);
 // dW_e[M, N] = A_e^T @ B_e over each local expert's rows (A [rows][M], B [rows][N];
 // b_blocked: B in the 32-column blocked layout of the backward's [dG | dU], n_max rows)
 hipError_t launch_grouped_gemm_tn(const void* src_a, const void* src_b, void* dw, const int32_t* offsets,
