@@ -161,7 +161,14 @@ moe_status moe_dispatch_indices_noalloc(const moe_shape* s, const int32_t* topk_
                                         int32_t* counts, int32_t* offsets, int32_t* perm,
                                         int32_t* pair_pos, hipStream_t stream);
 
-/* Bytes of device workspace moe_grouped_gemm needs for this shape (may be 0). */
+/* Bytes of device workspace the grouped GEMM calls take for this shape (may be
+ * 0). moe_grouped_gemm_gather(_save) use it for a copy of the gathered rows in
+ * 32-column blocks ([d/32][N_max][32]), whose K = 32 stages the gate/up loads
+ * read as contiguous runs: N_max * d * 2 bytes for bf16 when each row is read by
+ * at least 20 gate/up column tiles (d_ff / 128 >= 20) and the local experts
+ * average at least 128 rows (N_max / E_loc >= 128), 0 otherwise. Passing NULL
+ * instead makes those calls read the rows straight from x (same results, bit
+ * for bit). moe_grouped_gemm takes no workspace. */
 size_t moe_grouped_gemm_workspace_bytes(const moe_shape* s, moe_dtype dt);
 
 /* Grouped expert FFN over this rank's local experts: experts_forward of
@@ -179,7 +186,7 @@ size_t moe_grouped_gemm_workspace_bytes(const moe_shape* s, moe_dtype dt);
  *   w_down    [E_loc, d_ff, d] dt, read only.
  *   h         [N_max, d_ff] dt, written (intermediate activations).
  *   y         [N_max, d] dt, written: rows [0, N_loc).
- *   workspace moe_grouped_gemm_workspace_bytes(s, dt) bytes (may be NULL if 0).
+ *   workspace not used (may be NULL).
  * Uses s->T, d, d_ff, k, e_begin, e_end. */
 moe_status moe_grouped_gemm(const moe_shape* s, moe_dtype dt, const void* x_perm,
                             const int32_t* offsets, const void* w_gate_up,
@@ -188,8 +195,10 @@ moe_status moe_grouped_gemm(const moe_shape* s, moe_dtype dt, const void* x_perm
 
 /* moe_grouped_gemm with the dispatch's row gather folded into the gate/up
  * loads: the activation rows of local row r are x[perm[offsets[e_begin] + r] / k]
- * read directly from x, so x_perm is never written or read. Results (h, y) are
- * bit-identical to moe_dispatch + moe_grouped_gemm. Same sources as those two.
+ * read directly from x (or, with a workspace of moe_grouped_gemm_workspace_bytes
+ * > 0 bytes, from a blocked copy of them made first), so x_perm is never written
+ * or read. Results (h, y) are bit-identical to moe_dispatch + moe_grouped_gemm.
+ * Same sources as those two.
  *   x         [T, d] dt, read only: hidden states.
  *   perm      [T*k] int32 DEVICE array from moe_dispatch or moe_dispatch_indices.
  *   offsets, w_gate_up, w_down, h, y, workspace: as for moe_grouped_gemm

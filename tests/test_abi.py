@@ -198,6 +198,28 @@ def test_backward_entry_points_validate_on_the_host():
     assert lib.moe_grouped_gemm_backward_workspace_bytes(ctypes.byref(s), moe.MOE_F32) == 0
 
 
+def test_grouped_gemm_workspace_is_the_blocked_rows_when_they_pay():
+    """moe_grouped_gemm_workspace_bytes: N_max * d * 2 bytes (the gathered rows in
+    32-column blocks) for bf16 when d_ff / 128 >= 20 and N_max / E_loc >= 128;
+    0 otherwise, and for fp32."""
+    lib = moe.lib()
+    cases = [  # (T, d, d_ff, E, k, e_begin, e_end), blocked?
+        ((4096, 4096, 14336, 8, 2, 0, 8), True),        # dense8: 112 column tiles, 1024 rows per expert
+        ((8192, 2880, 2880, 128, 4, 0, 16), True),      # ep8_share128: 22, 2048
+        ((16384, 7168, 2048, 256, 8, 0, 32), False),    # skew256: 16 column tiles
+        ((32, 2880, 2880, 128, 4, 0, 128), False),      # decode32: 1 row per expert
+        ((600, 128, 2560, 8, 2, 0, 8), True),           # 20, 150
+        ((600, 128, 2528, 8, 2, 0, 8), False),          # 19 column tiles
+        ((500, 128, 2560, 8, 2, 0, 8), False),          # 125 rows per expert
+    ]
+    for (T, d, d_ff, E, k, lo, hi), blocked in cases:
+        s = moe.shape(T, d, d_ff, E, k, lo, hi)
+        n_max = T * min(k, hi - lo)
+        want = n_max * d * 2 if blocked else 0
+        assert lib.moe_grouped_gemm_workspace_bytes(ctypes.byref(s), moe.MOE_BF16) == want, (T, d, d_ff)
+        assert lib.moe_grouped_gemm_workspace_bytes(ctypes.byref(s), moe.MOE_F32) == 0
+
+
 # ----------------------------------------------------------------------------- debug build
 
 debug_built = pytest.mark.skipif(not os.path.exists(moe.debug_lib_path), reason="libmoe_debug.so not built")

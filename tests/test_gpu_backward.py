@@ -186,6 +186,8 @@ SAVED = [
      [129, 255, 256, 257, 288, 289, 300, 350, 400, 513, 544]),
     (mi.Workload("saved_split_to32", 80, 320, 160, 64, 1, 0, 64, "bf16", 49), [1, 16, 31, 32]),
     (mi.Workload("saved_split_to128", 293, 320, 160, 64, 1, 0, 64, "bf16", 50), [65, 100, 128]),
+    # gathered rows through their blocked copy (d_ff / 128 = 20 column tiles, N_max / E_loc = 150)
+    (mi.Workload("saved_blocked_rows", 600, 128, 2560, 8, 2, 0, 8, "bf16", 51), None),
 ]
 
 

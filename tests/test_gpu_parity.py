@@ -344,7 +344,10 @@ def test_layer_register_staged_kernel(w):
 
 FUSED = [SMALL[3], SMALL[4], SMALL[5],
          mi.Workload("fused_ragged_experts", 1100, 256, 160, 24, 3, 4, 20, "bf16", 25),
-         mi.Workload("fused_partial_range", 640, 192, 128, 16, 4, 6, 10, "bf16", 26)]
+         mi.Workload("fused_partial_range", 640, 192, 128, 16, 4, 6, 10, "bf16", 26),
+         # d_ff / 128 = 20 column tiles and N_max / E_loc = 150: the gathered rows go
+         # through their blocked copy (moe_grouped_gemm_workspace_bytes > 0)
+         mi.Workload("fused_blocked_rows", 600, 128, 2560, 8, 2, 0, 8, "bf16", 28)]
 
 
 @pytest.mark.parametrize("w", FUSED, ids=[w.name for w in FUSED])
@@ -367,10 +370,13 @@ def test_fused_layer_matches_oracle_and_staged_path(w):
     assert torch.equal(fused["out"], res["out"])
 
 
-def test_fused_layer_every_tile_height():
+@pytest.mark.parametrize("d_ff", [160, 2560], ids=["rows_gathered", "rows_blocked"])
+def test_fused_layer_every_tile_height(d_ff):
     counts = [0, 1, 31, 32, 33, 64, 65, 128, 129, 255, 256, 257, 288, 289, 300, 513, 544]
     E = len(counts)
-    w = mi.Workload("fused_tile_heights", int(sum(counts)), 256, 160, E, 1, 0, E, "bf16", 27)
+    w = mi.Workload("fused_tile_heights", int(sum(counts)), 256, d_ff, E, 1, 0, E, "bf16", 27)
+    s = moe.shape(w.T, w.d, w.d_ff, w.E, w.k, w.e_begin, w.e_end)
+    assert (moe.lib().moe_grouped_gemm_workspace_bytes(moe.ctypes.byref(s), moe.MOE_BF16) > 0) == (d_ff == 2560)
     logits = _one_hot_logits(counts, E, 27)
     res, ref = _layer_case(w, logits)
     x = mi.hidden_states(w)

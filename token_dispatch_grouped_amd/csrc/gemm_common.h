@@ -228,6 +228,14 @@ __device__ __forceinline__ int snake_tile(int i, int r, int G) {
 }
 
 
+// Byte offset of element (row, col) of a [rows][cols] bf16 matrix stored in
+// 32-column blocks of n_rows rows: block col / 32 holds [n_rows][32]. A K = 32
+// stage of a tile's rows is then one contiguous run, where row-major rows give
+// one 64-byte piece per row.
+__device__ __forceinline__ uint32_t blk_off(int row, int col, int n_rows) {
+  return static_cast<uint32_t>((col >> 5) * n_rows + row) * 64u + static_cast<uint32_t>(col & 31) * 2u;
+}
+
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
 // SiLU for results that are rounded to bf16 next: hardware exp2 and reciprocal,

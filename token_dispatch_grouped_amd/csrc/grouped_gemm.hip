@@ -324,7 +324,7 @@ hipError_t launch_grouped_gemm_bf16(const void* x_perm, const int32_t* offsets, 
   // 32-wide stages; other multiples of 8 take the register-staged kernel.
   if (d % 32 == 0 && d_ff % 32 == 0)
     return launch_grouped_gemm_lds(x_perm, nullptr, T, k, offsets, w_gu, w_dn, h, y, nullptr, d, d_ff, e_begin,
-                                   e_loc, n_max, g1, g2, stream);
+                                   e_loc, n_max, g1, g2, nullptr, stream);
   hipLaunchKernelGGL(grouped_gemm_bf16_kernel<true>, dim3(g1), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(x_perm), static_cast<const uint16_t*>(w_gu),
                      static_cast<uint16_t*>(h), offsets, e_begin, e_loc, d, d_ff, 2 * d_ff,
@@ -339,12 +339,12 @@ hipError_t launch_grouped_gemm_bf16(const void* x_perm, const int32_t* offsets, 
 hipError_t launch_grouped_gemm_gather(const void* x, const int32_t* perm, const int32_t* offsets,
                                       const void* w_gu, const void* w_dn, void* h, void* y, void* gu, int d,
                                       int d_ff, int e_begin, int e_loc, int64_t n_max, int64_t T, int k,
-                                      hipStream_t stream) {
+                                      void* a_blk, hipStream_t stream) {
   if (n_max == 0) return hipSuccess;
   const int g1 = grid_for(n_max, e_loc, kBM, (d_ff + 127) / 128, 1);
   const int g2 = grid_for(n_max, e_loc, kBM, (d + 255) / 256, 1);
   return launch_grouped_gemm_lds(x, perm, T, k, offsets, w_gu, w_dn, h, y, gu, d, d_ff, e_begin, e_loc, n_max, g1,
-                                 g2, stream);
+                                 g2, a_blk, stream);
 }
 
 hipError_t launch_grouped_gemm_f32(const float* x_perm, const int32_t* offsets, const float* w_gu,

@@ -68,11 +68,6 @@ struct Operand {
   int tail_stage;        // last rows, in stage tail_stage (-1: none)
 };
 
-// Byte offset of element (row, col) of a [rows][cols] matrix stored in 32-column
-// blocks of n_rows rows: block col / 32 holds [n_rows][32].
-__device__ __forceinline__ uint32_t blk_off(int row, int col, int n_rows) {
-  return static_cast<uint32_t>((col >> 5) * n_rows + row) * 64u + static_cast<uint32_t>(col & 31) * 2u;
-}
 
 // KROWS operand ([row][K], K contiguous) of ROWS rows (256 or 288): load j of a
 // stage covers rows 16j..16j+15, lane L row 16j + L/4, 16-byte chunk

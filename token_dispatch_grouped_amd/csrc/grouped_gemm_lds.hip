@@ -41,6 +41,11 @@
 //     their tiles, rounds walked in snake order, each XCD given a contiguous
 //     range of tile ids (gemm_common.h). Epilogue: bf16 buffer stores bounded by
 //     the tile's valid rows; SAVE also keeps the gate/up pre-activations.
+//   * Activation rows come as x_perm / H rows (64 bytes of each row per stage),
+//     gathered from x through perm in the loads, or, when each row is read by
+//     enough column tiles to pay for a copy, from a copy of the gathered rows in
+//     32-column blocks (gather_blocked_kernel), where a stage of a row tile is one
+//     contiguous run.
 #include <type_traits>
 
 #include "lds_pipe.h"
@@ -88,21 +93,25 @@ struct Layout {
   static_assert(BN == 256 || BN == 128, "full or half-width tiles");
 };
 
-// Where activation rows come from: rows of A in order (x_perm, H), or, with
-// GATHER, row r of the local segment is row perm_seg[r] / k of A (the token's
-// hidden state in x, the row gather of the dispatch done by the loads).
+// Where activation rows come from (AM): kAInOrder, rows of A in order (x_perm,
+// H); kAGather, row r of the local segment is row perm_seg[r] / k of A (the
+// token's hidden state in x, the row gather of the dispatch done by the loads);
+// kABlocked, row r of A stored in 32-column blocks of n_rows rows (blk_off).
+enum AMode { kAInOrder = 0, kAGather = 1, kABlocked = 2 };
 struct ARows {
   const int32_t* perm_seg;  // perm + offsets[e_begin]
   int k;
   uint32_t a_bytes;         // bytes of A (T * K * 2)
+  int n_rows;               // rows of a blocked A
 };
 
-template <bool SWIGLU, bool GATHER, bool SAVE, int H, int BN>
+template <bool SWIGLU, int AM, bool SAVE, int H, int BN>
 __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __restrict__ A,
                                           const uint16_t* __restrict__ Bexp, uint16_t* __restrict__ C,
                                           uint16_t* __restrict__ GU, int row0, int rows_valid, int n0, int K, int N,
                                           int ldb, const ARows& ar) {
   static_assert(!SAVE || SWIGLU, "pre-activations are kept only by the gate/up product");
+  constexpr bool GATHER = AM == kAGather, BLK = AM == kABlocked;
   using L = Layout<H, BN>;
   constexpr int MI = L::MI, NI = L::NI, WM = L::WM, WN = L::WN, PER = L::PER;
   // A half-width tile does half the MFMA work per stage, so the same lookahead
@@ -125,9 +134,13 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
   // logical chunk (L & 3) ^ ((row >> 2) & 3) into LDS slot L. Slots beyond the
   // A_INSTR instructions repeat an earlier instruction (identical bytes to the same
   // place), so every wave issues PER loads per stage.
-  const uint16_t* a_tile = GATHER ? A : A + static_cast<int64_t>(row0) * K;
+  // blocked: stage s of the tile's rows starts s * n_rows * 64 bytes after row0's first block
+  const uint16_t* a_tile = GATHER ? A : BLK ? A + static_cast<int64_t>(row0) * 32 : A + static_cast<int64_t>(row0) * K;
   const uint32_t a_bytes =
-      GATHER ? ar.a_bytes : static_cast<uint32_t>(rows_valid) * static_cast<uint32_t>(K) * 2u;
+      GATHER ? ar.a_bytes
+      : BLK  ? static_cast<uint32_t>(ar.n_rows) * static_cast<uint32_t>(K) * 2u - static_cast<uint32_t>(row0) * 64u
+             : static_cast<uint32_t>(rows_valid) * static_cast<uint32_t>(K) * 2u;
+  const uint32_t a_stage_bytes = BLK ? static_cast<uint32_t>(ar.n_rows) * 64u : kBK * 2u;
   const uint32_t b_bytes = static_cast<uint32_t>(K) * static_cast<uint32_t>(ldb) * 2u;
   uint32_t a_voff[L::A_PER_WAVE];
   int a_slot[L::A_PER_WAVE];
@@ -137,7 +150,10 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
     a_slot[jj] = j;
     const int r = 16 * j + (lane >> 2);
     const int c = (lane & 3) ^ ((lane >> 4) & 3);
-    if (GATHER) {
+    if (BLK) {
+      // rows past the tile's valid rows point past the buffer (zeros)
+      a_voff[jj] = r < rows_valid ? static_cast<uint32_t>(r) * 64u + static_cast<uint32_t>(c) * 16u : 0x80000000u;
+    } else if (GATHER) {
       // the token's row; rows past the tile's valid rows point past the buffer (zeros)
       const uint32_t src = r < rows_valid ? static_cast<uint32_t>(ar.perm_seg[row0 + r] / ar.k) * static_cast<uint32_t>(K) * 2u
                                           : 0x80000000u;
@@ -262,7 +278,8 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
   };
   auto stage_loads = [&](int s) {
     const int buf = s % NS;
-    return StageLoads{make_rsrc(a_tile + s * kBK, a_bytes - static_cast<uint32_t>(s) * kBK * 2u),
+    const uint32_t a_adv = static_cast<uint32_t>(s) * a_stage_bytes;
+    return StageLoads{make_rsrc(reinterpret_cast<const char*>(a_tile) + a_adv, a_bytes - a_adv),
                       make_rsrc(Bexp + static_cast<int64_t>(s) * kBK * ldb,
                                 b_bytes - static_cast<uint32_t>(s) * kBK * ldb * 2u),
                       sA_base + buf * kAStageBytes, sB_base + buf * kBBytes};
@@ -504,25 +521,25 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
 }
 
 // The tile height for rows_valid rows (a last row tile is the smallest that covers them).
-template <bool SWIGLU, bool GATHER, bool SAVE, int BN>
+template <bool SWIGLU, int AM, bool SAVE, int BN>
 __device__ __forceinline__ void run_tile(uint16_t* smem, const uint16_t* __restrict__ A,
                                          const uint16_t* __restrict__ Bexp, uint16_t* __restrict__ C,
                                          uint16_t* __restrict__ GU, int row0, int rows_valid, int n0, int K, int N,
                                          int ldb, const ARows& ar) {
   if (rows_valid > 256)
-    gemm_tile<SWIGLU, GATHER, SAVE, 288, BN>(smem, A, Bexp, C, GU, row0, rows_valid, n0, K, N, ldb, ar);
+    gemm_tile<SWIGLU, AM, SAVE, 288, BN>(smem, A, Bexp, C, GU, row0, rows_valid, n0, K, N, ldb, ar);
   else if (rows_valid > 128)
-    gemm_tile<SWIGLU, GATHER, SAVE, 256, BN>(smem, A, Bexp, C, GU, row0, rows_valid, n0, K, N, ldb, ar);
+    gemm_tile<SWIGLU, AM, SAVE, 256, BN>(smem, A, Bexp, C, GU, row0, rows_valid, n0, K, N, ldb, ar);
   else if (rows_valid > 64)
-    gemm_tile<SWIGLU, GATHER, SAVE, 128, BN>(smem, A, Bexp, C, GU, row0, rows_valid, n0, K, N, ldb, ar);
+    gemm_tile<SWIGLU, AM, SAVE, 128, BN>(smem, A, Bexp, C, GU, row0, rows_valid, n0, K, N, ldb, ar);
   else if (rows_valid > 32)
-    gemm_tile<SWIGLU, GATHER, SAVE, 64, BN>(smem, A, Bexp, C, GU, row0, rows_valid, n0, K, N, ldb, ar);
+    gemm_tile<SWIGLU, AM, SAVE, 64, BN>(smem, A, Bexp, C, GU, row0, rows_valid, n0, K, N, ldb, ar);
   else
-    gemm_tile<SWIGLU, GATHER, SAVE, 32, BN>(smem, A, Bexp, C, GU, row0, rows_valid, n0, K, N, ldb, ar);
+    gemm_tile<SWIGLU, AM, SAVE, 32, BN>(smem, A, Bexp, C, GU, row0, rows_valid, n0, K, N, ldb, ar);
 }
 
 // SAVE: the gate/up launch also writes its pre-activations [G | U] to GU.
-template <bool SWIGLU, bool GATHER, bool SAVE>
+template <bool SWIGLU, int AM, bool SAVE>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_lds_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
     uint16_t* __restrict__ GU, const int32_t* __restrict__ offsets, int e_begin, int e_loc, int K, int N, int ldb,
@@ -536,8 +553,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_lds_kernel(
   const int n_tiles = (N + kOutCols - 1) / kOutCols;
   const int total = uniform(tm.mstart[e_loc]) * n_tiles;
   const int64_t b_expert = static_cast<int64_t>(K) * ldb;
-  ARows ar{nullptr, k, a_bytes};
-  if (GATHER) ar.perm_seg = perm + offsets[e_begin];
+  ARows ar{nullptr, k, a_bytes, n_max};
+  if (AM == kAGather) ar.perm_seg = perm + offsets[e_begin];
 
   // Balance: when the last round would keep at most half of the workgroups busy
   // and every expert's tiles have the same height class (so that the rounds
@@ -581,49 +598,102 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_lds_kernel(
     const bool half = part != 0 || (narrow_last && tc.nt == n_tiles - 1 && rows_valid > 32);
     const uint16_t* Bexp = B + static_cast<int64_t>(tc.e) * b_expert;
     if (half)
-      run_tile<SWIGLU, GATHER, SAVE, 128>(smem, A, Bexp, C, GU, row0, rows_valid, n0, K, N, ldb, ar);
+      run_tile<SWIGLU, AM, SAVE, 128>(smem, A, Bexp, C, GU, row0, rows_valid, n0, K, N, ldb, ar);
     else
-      run_tile<SWIGLU, GATHER, SAVE, 256>(smem, A, Bexp, C, GU, row0, rows_valid, n0, K, N, ldb, ar);
+      run_tile<SWIGLU, AM, SAVE, 256>(smem, A, Bexp, C, GU, row0, rows_valid, n0, K, N, ldb, ar);
     // every wave has waited for its last LDS reads; the next tile's loads may land
     __builtin_amdgcn_s_barrier();
   }
 }
 
+// The local rows of x (row r = x[perm[offsets[e_begin] + r] / k]) into a_blk in
+// 32-column blocks of n_max rows (blk_off), for the gate/up launch to read as
+// contiguous stages. One 16-byte chunk of 8 columns per thread; eight
+// consecutive threads take rows 2m and 2m + 1 of one 32-column block (one
+// 128-byte line of the copy), the next eight the next block, so a wave reads two
+// whole 512-byte row pieces and writes eight whole lines.
+__global__ __launch_bounds__(kThreads) void gather_blocked_kernel(const uint4* __restrict__ x,
+                                                                  const int32_t* __restrict__ perm,
+                                                                  const int32_t* __restrict__ offsets,
+                                                                  uint16_t* __restrict__ a_blk, int e_begin, int e_end,
+                                                                  int k, int d, int n_max) {
+  const int seg0 = offsets[e_begin];
+  const int n_loc = min(offsets[e_end] - seg0, n_max);
+  const int nb = d / 32;
+  const int64_t items = static_cast<int64_t>((n_loc + 1) / 2) * nb * 8;
+  for (int64_t it = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; it < items;
+       it += static_cast<int64_t>(gridDim.x) * kThreads) {
+    const int sub = static_cast<int>(it & 3), rp = static_cast<int>((it >> 2) & 1);
+    const int64_t rest = it >> 3;
+    const int m = static_cast<int>(rest / nb), b = static_cast<int>(rest - static_cast<int64_t>(m) * nb);
+    const int r = 2 * m + rp;
+    if (r < n_loc) {
+      const int64_t tok = perm[seg0 + r] / k;
+      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(a_blk) + blk_off(r, b * 32 + sub * 8, n_max)) =
+          x[tok * (d / 8) + b * 4 + sub];
+    }
+  }
+}
+
 }  // namespace
+
+bool grouped_gemm_blocked_rows(int64_t n_max, int e_loc, int d, int d_ff) {
+  // Each gathered row is read by d_ff / 128 gate/up column tiles. Measured (one
+  // box): the copy paid on dense8 (112 tiles: gate/up -80 us for a 25 us copy)
+  // and ep8_share128 (23: -27 us for 12 us), not on skew256 (16: -67 us for 85
+  // us); tiles of few rows (decode) gain nothing. So: at least 20 column tiles,
+  // and at least 128 rows per local expert on average (by N_max), for d, d_ff
+  // multiples of 32 and a copy addressable in 31 bits.
+  return d % 32 == 0 && d_ff % 32 == 0 && d_ff / 128 >= 20 && e_loc > 0 && n_max / e_loc >= 128 &&
+         n_max * d * 2 + 64 <= INT32_MAX;
+}
 
 hipError_t launch_grouped_gemm_lds(const void* a, const int32_t* perm, int64_t T, int k, const int32_t* offsets,
                                    const void* w_gu, const void* w_dn, void* h, void* y, void* gu, int d, int d_ff,
                                    int e_begin, int e_loc, int64_t n_max, int grid_gate_up, int grid_down,
-                                   hipStream_t stream) {
+                                   void* a_blk, hipStream_t stream) {
   const uint16_t* wgu = static_cast<const uint16_t*>(w_gu);
   uint16_t* hh = static_cast<uint16_t*>(h);
   uint16_t* g = static_cast<uint16_t*>(gu);
-  if (perm != nullptr) {  // activation rows gathered from x by perm
+  const int nm = static_cast<int>(n_max);
+  if (perm != nullptr && a_blk != nullptr) {  // rows gathered into a blocked copy first
+    int64_t blocks = ((n_max + 1) / 2 * (d / 32) * 8 + kThreads - 1) / kThreads;
+    if (blocks > 8192) blocks = 8192;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(gather_blocked_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
+                       static_cast<const uint4*>(a), perm, offsets, static_cast<uint16_t*>(a_blk), e_begin,
+                       e_begin + e_loc, k, d, nm);
+    const uint16_t* ab = static_cast<const uint16_t*>(a_blk);
+    if (gu != nullptr)
+      hipLaunchKernelGGL((grouped_gemm_lds_kernel<true, kABlocked, true>), dim3(grid_gate_up), dim3(kThreads), 0,
+                         stream, ab, wgu, hh, g, offsets, e_begin, e_loc, d, d_ff, 2 * d_ff, nm, nullptr, k, 0u);
+    else
+      hipLaunchKernelGGL((grouped_gemm_lds_kernel<true, kABlocked, false>), dim3(grid_gate_up), dim3(kThreads), 0,
+                         stream, ab, wgu, hh, nullptr, offsets, e_begin, e_loc, d, d_ff, 2 * d_ff, nm, nullptr, k, 0u);
+  } else if (perm != nullptr) {  // activation rows gathered from x by perm in the loads
     const uint32_t a_bytes = static_cast<uint32_t>(T * d * 2);
     const uint16_t* x = static_cast<const uint16_t*>(a);
     if (gu != nullptr)
-      hipLaunchKernelGGL((grouped_gemm_lds_kernel<true, true, true>), dim3(grid_gate_up), dim3(kThreads), 0, stream,
-                         x, wgu, hh, g, offsets, e_begin, e_loc, d, d_ff, 2 * d_ff, static_cast<int>(n_max), perm, k,
-                         a_bytes);
+      hipLaunchKernelGGL((grouped_gemm_lds_kernel<true, kAGather, true>), dim3(grid_gate_up), dim3(kThreads), 0,
+                         stream, x, wgu, hh, g, offsets, e_begin, e_loc, d, d_ff, 2 * d_ff, nm, perm, k, a_bytes);
     else
-      hipLaunchKernelGGL((grouped_gemm_lds_kernel<true, true, false>), dim3(grid_gate_up), dim3(kThreads), 0, stream,
-                         x, wgu, hh, nullptr, offsets, e_begin, e_loc, d, d_ff, 2 * d_ff, static_cast<int>(n_max),
-                         perm, k, a_bytes);
+      hipLaunchKernelGGL((grouped_gemm_lds_kernel<true, kAGather, false>), dim3(grid_gate_up), dim3(kThreads), 0,
+                         stream, x, wgu, hh, nullptr, offsets, e_begin, e_loc, d, d_ff, 2 * d_ff, nm, perm, k,
+                         a_bytes);
   } else {
-    hipLaunchKernelGGL((grouped_gemm_lds_kernel<true, false, false>), dim3(grid_gate_up), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((grouped_gemm_lds_kernel<true, kAInOrder, false>), dim3(grid_gate_up), dim3(kThreads), 0, stream,
                        static_cast<const uint16_t*>(a), wgu, hh, nullptr, offsets, e_begin, e_loc, d, d_ff, 2 * d_ff,
-                       static_cast<int>(n_max), nullptr, k, 0u);
+                       nm, nullptr, k, 0u);
   }
-  hipLaunchKernelGGL((grouped_gemm_lds_kernel<false, false, false>), dim3(grid_down), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((grouped_gemm_lds_kernel<false, kAInOrder, false>), dim3(grid_down), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_dn),
-                     static_cast<uint16_t*>(y), nullptr, offsets, e_begin, e_loc, d_ff, d, d, static_cast<int>(n_max),
-                     nullptr, k, 0u);
+                     static_cast<uint16_t*>(y), nullptr, offsets, e_begin, e_loc, d_ff, d, d, nm, nullptr, k, 0u);
   return hipGetLastError();
 }
 
 hipError_t launch_grouped_gemm_plain(const void* a, const void* b, void* c, const int32_t* offsets, int e_begin,
                                      int e_loc, int K, int N, int ldb, int64_t n_max, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((grouped_gemm_lds_kernel<false, false, false>), dim3(grid), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((grouped_gemm_lds_kernel<false, kAInOrder, false>), dim3(grid), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), static_cast<uint16_t*>(c),
                      nullptr, offsets, e_begin, e_loc, K, N, ldb, static_cast<int>(n_max), nullptr, 1, 0u);
   return hipGetLastError();

@@ -130,9 +130,11 @@ moe_status moe_dispatch_indices_noalloc(const moe_shape* s, const int32_t* topk_
 }
 
 size_t moe_grouped_gemm_workspace_bytes(const moe_shape* s, moe_dtype dt) {
-  (void)s;
-  (void)dt;
-  return 0;
+  // the gathered rows' blocked copy of moe_grouped_gemm_gather(_save), when it pays
+  if (s == nullptr || dt != MOE_BF16 || s->e_end <= s->e_begin) return 0;
+  const int64_t n_max = n_max_of(s);
+  if (!moe::grouped_gemm_blocked_rows(n_max, s->e_end - s->e_begin, s->d, s->d_ff)) return 0;
+  return static_cast<size_t>(n_max) * static_cast<size_t>(s->d) * 2;
 }
 
 moe_status moe_grouped_gemm(const moe_shape* s, moe_dtype dt, const void* x_perm,
@@ -170,7 +172,8 @@ namespace {
 
 // moe_grouped_gemm_gather, and with gu != nullptr moe_grouped_gemm_gather_save
 moe_status gemm_gather(const moe_shape* s, moe_dtype dt, const void* x, const int32_t* perm, const int32_t* offsets,
-                       const void* w_gate_up, const void* w_down, void* h, void* y, void* gu, hipStream_t stream) {
+                       const void* w_gate_up, const void* w_down, void* h, void* y, void* gu, void* workspace,
+                       hipStream_t stream) {
   const moe_status st = check_shape(s, true);
   if (st != MOE_OK) return st;
   if (!valid_dtype(dt)) return MOE_EINVAL;
@@ -185,9 +188,11 @@ moe_status gemm_gather(const moe_shape* s, moe_dtype dt, const void* x, const in
   if ((static_cast<int64_t>(s->d) + 64) * 2 * s->d_ff * 2 > INT32_MAX ||
       (static_cast<int64_t>(s->d_ff) + 64) * s->d * 2 > INT32_MAX)
     return MOE_EUNSUPPORTED;
+  // the blocked copy of the gathered rows, when the workspace is there for it
+  void* a_blk = moe_grouped_gemm_workspace_bytes(s, dt) > 0 ? workspace : nullptr;
   return from_hip(moe::launch_grouped_gemm_gather(x, perm, offsets, w_gate_up, w_down, h, y, gu, s->d, s->d_ff,
                                                   s->e_begin, s->e_end - s->e_begin, n_max_of(s), s->T, s->k,
-                                                  stream));
+                                                  a_blk, stream));
 }
 
 }  // namespace
@@ -197,16 +202,14 @@ extern "C" {
 moe_status moe_grouped_gemm_gather(const moe_shape* s, moe_dtype dt, const void* x, const int32_t* perm,
                                    const int32_t* offsets, const void* w_gate_up, const void* w_down, void* h,
                                    void* y, void* workspace, hipStream_t stream) {
-  (void)workspace;
-  return gemm_gather(s, dt, x, perm, offsets, w_gate_up, w_down, h, y, nullptr, stream);
+  return gemm_gather(s, dt, x, perm, offsets, w_gate_up, w_down, h, y, nullptr, workspace, stream);
 }
 
 moe_status moe_grouped_gemm_gather_save(const moe_shape* s, moe_dtype dt, const void* x, const int32_t* perm,
                                         const int32_t* offsets, const void* w_gate_up, const void* w_down, void* h,
                                         void* y, void* gu, void* workspace, hipStream_t stream) {
-  (void)workspace;
   if (s != nullptr && s->T > 0 && gu == nullptr) return MOE_EINVAL;
-  return gemm_gather(s, dt, x, perm, offsets, w_gate_up, w_down, h, y, gu, stream);
+  return gemm_gather(s, dt, x, perm, offsets, w_gate_up, w_down, h, y, gu, workspace, stream);
 }
 
 moe_status moe_combine(const moe_shape* s, moe_dtype dt, const void* y, const int32_t* pair_pos,
