@@ -14,8 +14,9 @@ bracketed by a device synchronisation on both sides; `value` and `ms_per_step`
 use the median of the per-step event times. The same K steps back to back, with
 no flush, give `back_to_back_ms_per_step` (wall clock) for comparison.
 
-The roofline object covers the grouped GEMM (both of its MFMA launches), timed
-with events around it inside every timed step (median). The CPU baseline is
+The roofline object covers the grouped GEMM call (its two MFMA launches, and
+the blocked copy of the gathered rows that precedes them where the call makes
+one), timed with events around it inside every timed step (median). The CPU baseline is
 the fp64 oracle on a bounded sample of the same workload, timed on the host
 cores.
 """
@@ -388,10 +389,12 @@ def main() -> int:
         bound = "mfma" if w.dtype == "bf16" else "alu"
         achieved, peak, unit = flops / t_gemm / 1e12, peak_flops, "TFLOP/s"
     roofline = {
-        "kernel": ("moe_grouped_gemm_backward_saved (row gather, dH+SwiGLU backward, dX, dW_down, "
-                   "dW_gate_up launches; gate/up pre-activations kept by the forward)" if train else
+        "kernel": ("moe_grouped_gemm_backward_saved (row gather, blocked copy of dY, dH+SwiGLU "
+                   "backward, dX, dW_down, dW_gate_up launches; gate/up pre-activations kept by "
+                   "the forward)" if train else
                    ("moe_grouped_gemm_gather" if fused else "moe_grouped_gemm")
-                   + " (gate/up+SwiGLU launch, then down launch)"),
+                   + " (blocked copy of the gathered rows where the call makes one, gate/up+SwiGLU "
+                   "launch, then down launch)"),
         "bound": bound,
         "achieved": round(achieved, 2),
         "peak": peak,
