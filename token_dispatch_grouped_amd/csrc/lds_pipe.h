@@ -65,10 +65,15 @@ __device__ __forceinline__ i16x4_t ds_read_tr(uint32_t addr) {
   return v;
 }
 
+// Cache-policy field of a load: non-temporal. The caches treat the bytes as
+// streamed (read once) rather than keeping them for reuse.
+constexpr int kCpolNT = 2;
+
 // 16 bytes per lane from the buffer into LDS at lds_base + 16 * lane (lds_base is
-// a wave-uniform LDS byte address).
+// a wave-uniform LDS byte address), with cache policy CPOL (0 or kCpolNT).
+template <int CPOL = 0>
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS3 void*)(uintptr_t)lds_base, 16, voff, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS3 void*)(uintptr_t)lds_base, 16, voff, 0, 0, CPOL);
 }
 
 // c += a * b with c held in VGPRs
