@@ -424,16 +424,20 @@ def test_decode_shaped_skewed_layer_matches_oracle(w):
     assert torch.equal(fused["out"], res["out"])
 
 
-@pytest.mark.parametrize("T,k,E,lo,hi", [(600000, 8, 256, 0, 32), (16384, 8, 256, 0, 32), (70000, 4, 128, 16, 32),
-                                         (4096, 8, 256, 0, 32), (8193, 8, 1024, 1000, 1024), (257, 8, 16, 0, 8)],
+@pytest.mark.parametrize("T,k,E,lo,hi", [(600000, 8, 256, 0, 32), (40000, 4, 256, 0, 32), (70000, 4, 128, 16, 32),
+                                         (16384, 8, 256, 0, 32), (16385, 4, 512, 480, 512),
+                                         (16385, 4, 513, 480, 513),
+                                         (4096, 8, 256, 0, 32), (8192, 8, 1024, 1000, 1024), (257, 8, 16, 0, 8)],
                          ids=["four_launches_chunks_of_1024", "four_launches_chunks_of_256",
-                              "four_launches_chunks_of_256_ragged", "one_launch", "one_launch_largest",
+                              "four_launches_chunks_of_256_ragged", "two_launches_largest",
+                              "two_launches_smallest_ragged_most_experts", "four_launches_past_the_two_launch_experts", "one_launch", "one_launch_largest",
                               "one_launch_smallest"])
 def test_dispatch_every_path(T, k, E, lo, hi):
     """Every dispatch path gives the oracle's stable permutation: one launch per
-    1024 pairs up to 65536 pairs (above the single-workgroup 2048), then four
-    launches with 256-pair chunks, switching to 1024-pair chunks once the
-    (expert, chunk) tables would pass 4M entries."""
+    1024 pairs up to 65536 pairs (above the single-workgroup 2048), then two
+    launches (chunk counts, then scan and scatter per 512 pairs) up to 131072
+    pairs and 512 experts, then four launches with 256-pair chunks, switching
+    to 1024-pair chunks once the (expert, chunk) tables would pass 4M entries."""
     rng = np.random.default_rng(T + k + E)
     idx_np = rng.integers(0, E, size=(T, k)).astype(np.int32)
     x = torch.empty((T, 8), dtype=torch.bfloat16, device="cuda")
@@ -488,8 +492,8 @@ def test_layers_on_two_streams_from_two_threads():
 
 # ----------------------------------------------------------------------------- debug build
 
-@pytest.mark.parametrize("T,E,k", [(300, 8, 2), (3000, 64, 4), (20000, 64, 4), (0, 16, 2)],
-                         ids=["one_workgroup", "one_launch", "four_launches", "empty"])
+@pytest.mark.parametrize("T,E,k", [(300, 8, 2), (3000, 64, 4), (20000, 64, 4), (40000, 64, 4), (0, 16, 2)],
+                         ids=["one_workgroup", "one_launch", "two_launches", "four_launches", "empty"])
 def test_debug_build_refuses_out_of_range_ids(T, E, k):
     """libmoe_debug.so counts the ids outside [0, E) on the device and the binding
     refuses them; valid ids give the release build's results bit for bit."""

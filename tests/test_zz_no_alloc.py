@@ -38,7 +38,7 @@ def _run(name, T, k, E, lo, hi, idx, out, ws=None):
 
 
 @pytest.mark.parametrize("shapes", [
-    [(16384, 8, 256, 0, 32), (700, 4, 128, 16, 32), (300, 2, 8, 0, 8)],  # chunked, chunked, one workgroup
+    [(16384, 8, 256, 0, 32), (700, 4, 128, 16, 32), (300, 2, 8, 0, 8)],  # two launches, one launch, one workgroup
 ], ids=["large_then_smaller"])
 def test_noalloc_matches_dispatch_indices(shapes):
     for T, k, E, lo, hi in shapes:

@@ -12,6 +12,9 @@
 //   P <= 2048  : one workgroup does everything (dispatch_small_kernel);
 //   P <= 65536 : one launch, a workgroup per 1024 pairs that counts every pair
 //                itself (dispatch_onepass_kernel);
+//   P <= 131072: two launches (E < 512), per-chunk histograms of 2048 pairs,
+//                then a workgroup per 512 pairs that scans the whole table and
+//                places its pairs (dispatch_scan_scatter_kernel);
 //   larger     : four launches over per-chunk histograms in the workspace:
 //   1. count   : one workgroup per chunk of 256 (or 1024) flat pairs builds an
 //                LDS histogram and stores it expert-major: ws[e * n_chunks + c].
@@ -46,7 +49,9 @@ constexpr int kDebugRows = 0;
 // ints before the histogram tables: the debug error word, padded to 256 bytes
 constexpr int kWsHead = kDebugRows * 64;
 
-template <int CHUNK>
+// CMAJOR: the table is stored chunk-major, ws[chunk * rows + e], for the
+// two-launch path, whose scan reads one expert's counts per thread.
+template <int CHUNK, bool CMAJOR = false>
 __global__ __launch_bounds__(kThreads) void dispatch_count_kernel(const int32_t* __restrict__ idx,
                                                                   int32_t* __restrict__ ws,
                                                                   int64_t P, int E, int n_chunks) {
@@ -65,7 +70,8 @@ __global__ __launch_bounds__(kThreads) void dispatch_count_kernel(const int32_t*
   }
   __syncthreads();
   for (int e = threadIdx.x; e < rows; e += kThreads)
-    ws[static_cast<int64_t>(e) * n_chunks + blockIdx.x] = hist[e];
+    ws[CMAJOR ? static_cast<int64_t>(blockIdx.x) * rows + e : static_cast<int64_t>(e) * n_chunks + blockIdx.x] =
+        hist[e];
 }
 
 constexpr int kScanWavesPerBlock = kThreads / kWave;
@@ -447,6 +453,123 @@ __global__ __launch_bounds__(kSmallThreads) void dispatch_onepass_kernel(
   }
 }
 
+// Past kOnePassPairs, up to kFusedPairs pairs and kFusedThreads table rows (E,
+// plus the debug row): two launches. The count launch
+// stores a histogram per chunk of kFusedChunk pairs (at most kWave chunks),
+// chunk-major. Then one workgroup per kFusedSub pairs (a quarter of a chunk, so
+// that every CU ranks pairs) reads the whole table from L2 (rows x n_chunks x 4
+// bytes, 64 KB at E = 256): a thread per expert loads that expert's count in
+// every chunk at once and adds them, the total and the part before its chunk.
+// It counts the pairs of its chunk before its quarter itself (at most 1536 ids,
+// in LDS), scans the totals into offsets (workgroup 0 writes counts and
+// offsets) and places its pairs by the same stable ballot ranking as the other
+// paths. This folds the totals and bases launches of the larger path into the
+// scatter.
+constexpr int kFusedChunk = 2048;
+constexpr int kFusedSub = 512;
+constexpr int kFusedThreads = 512;
+constexpr int64_t kFusedPairs = static_cast<int64_t>(kFusedChunk) * kWave;
+
+__global__ __launch_bounds__(kFusedThreads) void dispatch_scan_scatter_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ ws, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ pair_pos,
+    int32_t* __restrict__ err_word, int P, int E, int n_chunks, int e_begin, int e_end) {
+  constexpr int kWaves = kFusedThreads / kWave;
+  constexpr int kSubs = kFusedChunk / kFusedSub;     // quarters per chunk
+  constexpr int kBefore = kFusedSub * (kSubs - 1) / kFusedThreads;  // ids before the quarter, per thread
+  __shared__ int run[kMaxExperts];          // pairs before this quarter, then its next slot per expert
+  __shared__ int tot[kMaxExperts + 1];      // the offsets
+  __shared__ int wsum[kWaves];              // per-wave sums of the totals
+  __shared__ int wcnt[kWaves][kMaxExperts]; // per-wave counts
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wv = tid / kWave;
+  const int sub = blockIdx.x;
+  const int chunk = sub / kSubs;
+  const int c0 = chunk * kFusedChunk;        // the chunk's first pair
+  const int q0 = sub * kFusedSub;            // the quarter's first pair
+  const uint64_t lt_mask = (uint64_t{1} << lane) - 1;
+  const int p = q0 + tid;
+  const int e = p < P ? idx[p] : -1;
+  int prev[kBefore];                         // ids of the chunk before the quarter
+#pragma unroll
+  for (int u = 0; u < kBefore; ++u) {
+    const int q = c0 + u * kFusedThreads + tid;
+    prev[u] = q < q0 ? idx[q] : -1;
+  }
+  // thread x holds expert x's count in every chunk (rows <= kFusedThreads), loaded
+  // with the ids, before the first barrier
+  const int rows = E + kDebugRows;
+  const int x = tid;
+  int v[kWave];
+#pragma unroll
+  for (int c = 0; c < kWave; ++c) v[c] = x < rows && c < n_chunks ? ws[static_cast<int64_t>(c) * rows + x] : 0;
+  if (x < E) run[x] = 0;
+  for (int i = tid; i < kWaves * E; i += kFusedThreads) wcnt[i / E][i % E] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kBefore; ++u)
+    if (static_cast<unsigned>(prev[u]) < static_cast<unsigned>(E)) atomicAdd(&run[prev[u]], 1);
+  int all = 0, before = 0;
+#pragma unroll
+  for (int c = 0; c < kWave; ++c) {
+    all += v[c];
+    before += c < chunk ? v[c] : 0;
+  }
+  if (kDebugRows && x == E && sub == 0) err_word[0] = all;  // ids outside [0, E)
+  // exclusive scan of the totals over the workgroup: a scan inside each wave,
+  // then the sums of the waves before
+  const int cnt = x < E ? all : 0;
+  int incl = cnt;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == kWave - 1) wsum[wv] = incl;
+  __syncthreads();
+  int first = incl - cnt, grand = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < kWaves; ++w2) {
+    first += w2 < wv ? wsum[w2] : 0;
+    grand += wsum[w2];
+  }
+  if (x < E) {
+    if (sub == 0) {
+      counts[x] = cnt;
+      offsets[x] = first;
+    }
+    tot[x] = first;
+    run[x] += first + before;  // the quarter's first slot of expert x
+  }
+  if (x == 0) {
+    tot[E] = grand;
+    if (sub == 0) offsets[E] = grand;
+  }
+  __syncthreads();
+  const int seg0 = tot[e_begin];
+  const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(E);
+  if (p < P && !valid) pair_pos[p] = -1;
+  uint64_t remaining = __ballot(valid);
+  uint64_t peers = 0;
+  while (remaining) {
+    const int leader = __ffsll(static_cast<unsigned long long>(remaining)) - 1;
+    const int le = __builtin_amdgcn_readlane(e, leader);
+    const uint64_t m = __ballot(valid && e == le);
+    if (valid && e == le) peers = m;
+    remaining &= ~m;
+  }
+  const int rank = __popcll(peers & lt_mask);
+  if (valid && rank == 0) wcnt[wv][e] = __popcll(peers);
+  __syncthreads();
+  if (valid) {
+    int pos = run[e] + rank;
+    for (int w2 = 0; w2 < wv; ++w2) pos += wcnt[w2][e];
+    perm[pos] = p;
+    pair_pos[p] = (e >= e_begin && e < e_end) ? pos - seg0 : -1;
+  }
+}
+
 // Rows are copied in parts of kGatherVec 16-byte vectors (2 per lane), one part
 // per wave at a time, so that a few long rows still spread over many waves. Two
 // per lane, with more parts and waves, measured faster than 4 or 8 on every
@@ -548,10 +671,20 @@ hipError_t launch_dispatch(const void* x, size_t row_bytes, const int32_t* idx, 
     if (x_perm == nullptr) return hipGetLastError();
     return launch_gather_rows(x, row_bytes, perm, offsets, x_perm, k, e_begin, e_end, n_max, stream);
   }
+  int32_t* ws = static_cast<int32_t*>(workspace) + kWsHead;
+  if (P > kOnePassPairs && P <= kFusedPairs && E + kDebugRows <= kFusedThreads) {
+    const int n_fused = static_cast<int>((P + kFusedChunk - 1) / kFusedChunk);
+    hipLaunchKernelGGL((dispatch_count_kernel<kFusedChunk, true>), dim3(n_fused), dim3(kThreads), 0, stream, idx, ws,
+                       P, E, n_fused);
+    const int n_subs = static_cast<int>((P + kFusedSub - 1) / kFusedSub);
+    hipLaunchKernelGGL(dispatch_scan_scatter_kernel, dim3(n_subs), dim3(kFusedThreads), 0, stream, idx, ws, counts,
+                       offsets, perm, pair_pos, err_word, static_cast<int>(P), E, n_fused, e_begin, e_end);
+    if (x_perm == nullptr) return hipGetLastError();
+    return launch_gather_rows(x, row_bytes, perm, offsets, x_perm, k, e_begin, e_end, n_max, stream);
+  }
   const int chunk = dispatch_chunk(P, E);
   const int n_chunks = static_cast<int>((P + chunk - 1) / chunk);
   const int rows = E + kDebugRows;
-  int32_t* ws = static_cast<int32_t*>(workspace) + kWsHead;
   if (n_chunks > 0) {
     if (chunk == 256)
       hipLaunchKernelGGL(dispatch_count_kernel<256>, dim3(n_chunks), dim3(kThreads), 0, stream, idx, ws, P, E,
