@@ -65,10 +65,6 @@ __device__ __forceinline__ i16x4_t ds_read_tr(uint32_t addr) {
   return v;
 }
 
-// Cache-policy field of a load: non-temporal. The caches treat the bytes as
-// streamed (read once) rather than keeping them for reuse.
-constexpr int kCpolNT = 2;
-
 // 16 bytes per lane from the buffer into LDS at lds_base + 16 * lane (lds_base is
 // a wave-uniform LDS byte address), with cache policy CPOL (0 or kCpolNT).
 template <int CPOL = 0>

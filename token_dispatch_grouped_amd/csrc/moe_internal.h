@@ -36,8 +36,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
+// Cache-policy field of a load: non-temporal. The caches treat the bytes as
+// streamed (read once) rather than keeping them for reuse.
+constexpr int kCpolNT = 2;
+
+// 16 bytes at voffset, with cache policy CPOL (0 or kCpolNT).
+template <int CPOL = 0>
 __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset) {
-  const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, static_cast<int>(voffset), 0, 0);
+  const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, static_cast<int>(voffset), 0, CPOL);
   return make_uint4(static_cast<uint32_t>(v.x), static_cast<uint32_t>(v.y), static_cast<uint32_t>(v.z),
                     static_cast<uint32_t>(v.w));
 }
