@@ -164,11 +164,13 @@ moe_status moe_dispatch_indices_noalloc(const moe_shape* s, const int32_t* topk_
 /* Bytes of device workspace the grouped GEMM calls take for this shape (may be
  * 0). moe_grouped_gemm_gather(_save) use it for a copy of the gathered rows in
  * 32-column blocks ([d/32][N_max][32]), whose K = 32 stages the gate/up loads
- * read as contiguous runs: N_max * d * 2 bytes for bf16 when each row is read by
- * at least 20 gate/up column tiles (d_ff / 128 >= 20) and the local experts
- * average at least 128 rows (N_max / E_loc >= 128), 0 otherwise. Passing NULL
- * instead makes those calls read the rows straight from x (same results, bit
- * for bit). moe_grouped_gemm takes no workspace. */
+ * read as contiguous runs, followed by 1 KB of per-XCD tile counts that pace the
+ * gate/up launch's workgroups (cleared by the call itself): N_max * d * 2 + 1024
+ * bytes for bf16 when each row is read by at least 20 gate/up column tiles
+ * (d_ff / 128 >= 20) and the local experts average at least 128 rows
+ * (N_max / E_loc >= 128), 0 otherwise. Passing NULL instead makes those calls
+ * read the rows straight from x (same results, bit for bit). Calls that overlap
+ * on one workspace race. moe_grouped_gemm takes no workspace. */
 size_t moe_grouped_gemm_workspace_bytes(const moe_shape* s, moe_dtype dt);
 
 /* Grouped expert FFN over this rank's local experts: experts_forward of

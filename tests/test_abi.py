@@ -200,8 +200,8 @@ def test_backward_entry_points_validate_on_the_host():
 
 def test_grouped_gemm_workspace_is_the_blocked_rows_when_they_pay():
     """moe_grouped_gemm_workspace_bytes: N_max * d * 2 bytes (the gathered rows in
-    32-column blocks) for bf16 when d_ff / 128 >= 20 and N_max / E_loc >= 128;
-    0 otherwise, and for fp32."""
+    32-column blocks) plus 1 KB of per-XCD tile counts for bf16 when d_ff / 128 >= 20
+    and N_max / E_loc >= 128; 0 otherwise, and for fp32."""
     lib = moe.lib()
     cases = [  # (T, d, d_ff, E, k, e_begin, e_end), blocked?
         ((4096, 4096, 14336, 8, 2, 0, 8), True),        # dense8: 112 column tiles, 1024 rows per expert
@@ -215,7 +215,7 @@ def test_grouped_gemm_workspace_is_the_blocked_rows_when_they_pay():
     for (T, d, d_ff, E, k, lo, hi), blocked in cases:
         s = moe.shape(T, d, d_ff, E, k, lo, hi)
         n_max = T * min(k, hi - lo)
-        want = n_max * d * 2 if blocked else 0
+        want = n_max * d * 2 + 1024 if blocked else 0
         assert lib.moe_grouped_gemm_workspace_bytes(ctypes.byref(s), moe.MOE_BF16) == want, (T, d, d_ff)
         assert lib.moe_grouped_gemm_workspace_bytes(ctypes.byref(s), moe.MOE_F32) == 0
 

@@ -57,6 +57,8 @@ using namespace gemm;
 
 constexpr int kBK = 32;                       // K per stage
 constexpr int kStages = 4;
+constexpr int kPaceStride = 32;  // ints between the per-XCD tile counts (one 128-byte line each)
+constexpr int kPacePolls = 64;
 constexpr int kARows = 288;                   // rows an activation stage holds
 constexpr int kAStageElems = kARows * kBK;    // 18 KB
 constexpr int kBStageElems = 256 * kBK;       // 16 KB
@@ -547,7 +549,7 @@ template <bool SWIGLU, int AM, bool SAVE>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_lds_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
     uint16_t* __restrict__ GU, const int32_t* __restrict__ offsets, int e_begin, int e_loc, int K, int N, int ldb,
-    int n_max, const int32_t* __restrict__ perm, int k, uint32_t a_bytes) {
+    int n_max, const int32_t* __restrict__ perm, int k, uint32_t a_bytes, int* __restrict__ xcd_done) {
   __shared__ __attribute__((aligned(1024))) uint16_t smem[kStages * (kAStageElems + kBStageElems)];
   __shared__ SortedTileMap tm;
   // a remainder of at most 32 rows rides on the expert's last full tile (288 rows)
@@ -578,6 +580,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_lds_kernel(
   const int n_split = uniform(tm.classes) == 1 ? last : tall_last;  // last-round tiles split in two
   const bool split = total > 0 && n_split > 0 && last + n_split <= G;
   const bool narrow_last = N - (n_tiles - 1) * kOutCols <= kOutCols / 2;
+  // Pacing (blocked activation rows, forward only): the rows of a blocked copy
+  // arrive fast enough that the workgroups of one XCD drift apart by more k-steps
+  // than its L2 holds, and re-fetch their round's shared rows and weight panels.
+  // A workgroup that runs a tile ahead of most of its XCD waits at the tile
+  // boundary. xcd_done holds one count per XCD, zeroed by the copy kernel.
+  const bool pace = AM == kABlocked && !SAVE && xcd_done != nullptr && (G & 7) == 0;
+  const int per_xcd = G >> 3;
   for (int i = 0;; ++i) {
     int tile, part = 0;  // part: 0 the whole tile, 1 or 2 its first or second half
     if (split && i == rounds - 1) {
@@ -592,6 +601,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_lds_kernel(
     } else {
       tile = snake_tile(i, r, G);
       if (tile >= total) break;  // later rounds hold only larger ids
+    }
+    if (pace && i > 0 && uniform(static_cast<int>(threadIdx.x)) < kWave) {
+      // this workgroup has finished i tiles: count it, then wait (a bounded number
+      // of polls) until all but a quarter of its XCD's workgroups have as well
+      int* ctr = xcd_done + (blockIdx.x & 7) * kPaceStride;
+      int seen = 0;
+      if (lane_id() == 0) seen = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+      seen = __builtin_amdgcn_readfirstlane(seen);
+      for (int poll = 0; poll < kPacePolls && seen < i * per_xcd - per_xcd / 4; ++poll) {
+        __builtin_amdgcn_s_sleep(4);
+        seen = __builtin_amdgcn_readfirstlane(__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      }
     }
     const SortedTile tc = find_sorted_tile(tm, tile, n_tiles, e_loc);
     const int row0 = uniform(tm.rstart[tc.e]) + tc.mt * 256;
@@ -616,6 +637,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_lds_kernel(
     // every wave has waited for its last LDS reads; the next tile's loads may land
     __builtin_amdgcn_s_barrier();
   }
+  // done: no workgroup of this XCD waits for this one any more
+  if (pace && threadIdx.x == 0)
+    __hip_atomic_fetch_add(xcd_done + (blockIdx.x & 7) * kPaceStride, 1 << 24, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The local rows of x (row r = x[perm[offsets[e_begin] + r] / k]) into a_blk in
@@ -628,7 +653,8 @@ __global__ __launch_bounds__(kThreads) void gather_blocked_kernel(const uint4* _
                                                                   const int32_t* __restrict__ perm,
                                                                   const int32_t* __restrict__ offsets,
                                                                   uint16_t* __restrict__ a_blk, int e_begin, int e_end,
-                                                                  int k, int d, int n_max) {
+                                                                  int k, int d, int n_max, int* __restrict__ xcd_done) {
+  if (blockIdx.x == 0 && threadIdx.x < 8) xcd_done[threadIdx.x * kPaceStride] = 0;  // for the gate/up launch
   const int seg0 = offsets[e_begin];
   const int n_loc = min(offsets[e_end] - seg0, n_max);
   const int nb = d / 32;
@@ -648,6 +674,12 @@ __global__ __launch_bounds__(kThreads) void gather_blocked_kernel(const uint4* _
 }
 
 }  // namespace
+
+size_t blocked_rows_bytes(int64_t n_max, int d) { return static_cast<size_t>(n_max) * d * 2; }
+
+size_t blocked_rows_workspace_bytes(int64_t n_max, int d) {
+  return blocked_rows_bytes(n_max, d) + 8 * kPaceStride * sizeof(int);
+}
 
 bool grouped_gemm_blocked_rows(int64_t n_max, int e_loc, int d, int d_ff) {
   // Each gathered row is read by d_ff / 128 gate/up column tiles. Measured (one
@@ -672,34 +704,40 @@ hipError_t launch_grouped_gemm_lds(const void* a, const int32_t* perm, int64_t T
     int64_t blocks = ((n_max + 1) / 2 * (d / 32) * 8 + kThreads - 1) / kThreads;
     if (blocks > 8192) blocks = 8192;
     if (blocks < 1) blocks = 1;
+    // the per-XCD tile counts of the pacing follow the copy in the workspace
+    int* xcd_done = reinterpret_cast<int*>(static_cast<char*>(a_blk) + blocked_rows_bytes(n_max, d));
     hipLaunchKernelGGL(gather_blocked_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
                        static_cast<const uint4*>(a), perm, offsets, static_cast<uint16_t*>(a_blk), e_begin,
-                       e_begin + e_loc, k, d, nm);
+                       e_begin + e_loc, k, d, nm, xcd_done);
     const uint16_t* ab = static_cast<const uint16_t*>(a_blk);
     if (gu != nullptr)
       hipLaunchKernelGGL((grouped_gemm_lds_kernel<true, kABlocked, true>), dim3(grid_gate_up), dim3(kThreads), 0,
-                         stream, ab, wgu, hh, g, offsets, e_begin, e_loc, d, d_ff, 2 * d_ff, nm, nullptr, k, 0u);
+                         stream, ab, wgu, hh, g, offsets, e_begin, e_loc, d, d_ff, 2 * d_ff, nm, nullptr, k, 0u,
+                         nullptr);
     else
       hipLaunchKernelGGL((grouped_gemm_lds_kernel<true, kABlocked, false>), dim3(grid_gate_up), dim3(kThreads), 0,
-                         stream, ab, wgu, hh, nullptr, offsets, e_begin, e_loc, d, d_ff, 2 * d_ff, nm, nullptr, k, 0u);
+                         stream, ab, wgu, hh, nullptr, offsets, e_begin, e_loc, d, d_ff, 2 * d_ff, nm, nullptr, k, 0u,
+                         xcd_done);
   } else if (perm != nullptr) {  // activation rows gathered from x by perm in the loads
     const uint32_t a_bytes = static_cast<uint32_t>(T * d * 2);
     const uint16_t* x = static_cast<const uint16_t*>(a);
     if (gu != nullptr)
       hipLaunchKernelGGL((grouped_gemm_lds_kernel<true, kAGather, true>), dim3(grid_gate_up), dim3(kThreads), 0,
-                         stream, x, wgu, hh, g, offsets, e_begin, e_loc, d, d_ff, 2 * d_ff, nm, perm, k, a_bytes);
+                         stream, x, wgu, hh, g, offsets, e_begin, e_loc, d, d_ff, 2 * d_ff, nm, perm, k, a_bytes,
+                         nullptr);
     else
       hipLaunchKernelGGL((grouped_gemm_lds_kernel<true, kAGather, false>), dim3(grid_gate_up), dim3(kThreads), 0,
                          stream, x, wgu, hh, nullptr, offsets, e_begin, e_loc, d, d_ff, 2 * d_ff, nm, perm, k,
-                         a_bytes);
+                         a_bytes, nullptr);
   } else {
     hipLaunchKernelGGL((grouped_gemm_lds_kernel<true, kAInOrder, false>), dim3(grid_gate_up), dim3(kThreads), 0, stream,
                        static_cast<const uint16_t*>(a), wgu, hh, nullptr, offsets, e_begin, e_loc, d, d_ff, 2 * d_ff,
-                       nm, nullptr, k, 0u);
+                       nm, nullptr, k, 0u, nullptr);
   }
   hipLaunchKernelGGL((grouped_gemm_lds_kernel<false, kAInOrder, false>), dim3(grid_down), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_dn),
-                     static_cast<uint16_t*>(y), nullptr, offsets, e_begin, e_loc, d_ff, d, d, nm, nullptr, k, 0u);
+                     static_cast<uint16_t*>(y), nullptr, offsets, e_begin, e_loc, d_ff, d, d, nm, nullptr, k, 0u,
+                     nullptr);
   return hipGetLastError();
 }
 
@@ -707,7 +745,7 @@ hipError_t launch_grouped_gemm_plain(const void* a, const void* b, void* c, cons
                                      int e_loc, int K, int N, int ldb, int64_t n_max, int grid, hipStream_t stream) {
   hipLaunchKernelGGL((grouped_gemm_lds_kernel<false, kAInOrder, false>), dim3(grid), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), static_cast<uint16_t*>(c),
-                     nullptr, offsets, e_begin, e_loc, K, N, ldb, static_cast<int>(n_max), nullptr, 1, 0u);
+                     nullptr, offsets, e_begin, e_loc, K, N, ldb, static_cast<int>(n_max), nullptr, 1, 0u, nullptr);
   return hipGetLastError();
 }
 

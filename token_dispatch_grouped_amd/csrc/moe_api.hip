@@ -134,7 +134,7 @@ size_t moe_grouped_gemm_workspace_bytes(const moe_shape* s, moe_dtype dt) {
   if (s == nullptr || dt != MOE_BF16 || s->e_end <= s->e_begin) return 0;
   const int64_t n_max = n_max_of(s);
   if (!moe::grouped_gemm_blocked_rows(n_max, s->e_end - s->e_begin, s->d, s->d_ff)) return 0;
-  return static_cast<size_t>(n_max) * static_cast<size_t>(s->d) * 2;
+  return moe::blocked_rows_workspace_bytes(n_max, s->d);
 }
 
 moe_status moe_grouped_gemm(const moe_shape* s, moe_dtype dt, const void* x_perm,

@@ -73,14 +73,18 @@ hipError_t launch_grouped_gemm_bf16(const void* x_perm, const int32_t* offsets, 
                                     int e_loc, int64_t n_max, int64_t T, int k, int E,
                                     hipStream_t stream);
 // a = x_perm (perm == nullptr) or x, whose rows the gate/up loads gather through perm (or, with a_blk,
-// a copy of them gathered into a_blk in 32-column blocks of n_max rows first);
+// a copy of them gathered into a_blk in 32-column blocks of n_max rows first; a_blk then has
+// blocked_rows_workspace_bytes(n_max, d) bytes);
 // gu != nullptr (with perm only): the gate/up pre-activations [G | U] are written there too
 hipError_t launch_grouped_gemm_lds(const void* a, const int32_t* perm, int64_t T, int k, const int32_t* offsets,
                                    const void* w_gu, const void* w_dn, void* h, void* y, void* gu, int d, int d_ff,
                                    int e_begin, int e_loc, int64_t n_max, int grid_gate_up, int grid_down,
                                    void* a_blk, hipStream_t stream);
-// Whether the gathered gate/up rows are copied in 32-column blocks first (n_max * d * 2 bytes of workspace)
+// Whether the gathered gate/up rows are copied in 32-column blocks first; the workspace then holds
+// the copy (blocked_rows_bytes) and, after it, one tile count per XCD for the gate/up launch's pacing
 bool grouped_gemm_blocked_rows(int64_t n_max, int e_loc, int d, int d_ff);
+size_t blocked_rows_bytes(int64_t n_max, int d);
+size_t blocked_rows_workspace_bytes(int64_t n_max, int d);
 // Gate/up rows gathered from x through perm, no x_perm (bf16, d and d_ff multiples of 32);
 // gu != nullptr: [G | U] of every local row is kept there as well; a_blk: see launch_grouped_gemm_lds.
 hipError_t launch_grouped_gemm_gather(const void* x, const int32_t* perm, const int32_t* offsets,
