@@ -389,6 +389,35 @@ def test_fused_layer_every_tile_height(d_ff):
     assert torch.equal(fused["out"], res["out"])
 
 
+def test_fused_gemm_workspace_contents_do_not_matter():
+    """The blocked-rows workspace also holds the per-XCD tile counts that pace the
+    gate/up workgroups; the call clears them itself. With the workspace filled with
+    0xFF bytes, and again on the counts the first call left, H and Y equal the
+    staged path's (the oracle-checked layer) bit for bit. 2 row tiles x 20 column
+    tiles x 8 experts = 320 tiles, more than one round, so the pacing waits."""
+    import ctypes
+    w = mi.Workload("fused_paced", 2048, 128, 2560, 8, 2, 0, 8, "bf16", 29)
+    res, ref = _layer_case(w)
+    s = moe.shape(w.T, w.d, w.d_ff, w.E, w.k, w.e_begin, w.e_end)
+    ws_bytes = moe.lib().moe_grouped_gemm_workspace_bytes(ctypes.byref(s), moe.MOE_BF16)
+    assert ws_bytes == w.n_max * w.d * 2 + 1024
+    x = g.to_dev(mi.hidden_states(w), w.dtype)
+    wgu, wdn = (g.to_dev(a, w.dtype) for a in mi.expert_weights(w))
+    ws = torch.full((ws_bytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    n_loc = ref["x_perm"].shape[0]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    for call in range(2):
+        h = torch.full((w.n_max, w.d_ff), float("nan"), dtype=torch.bfloat16, device="cuda")
+        y = torch.full((w.n_max, w.d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        st = moe.lib().moe_grouped_gemm_gather(ctypes.byref(s), moe.MOE_BF16, p(x), p(res["perm"]),
+                                               p(res["offsets"]), p(wgu), p(wdn), p(h), p(y), p(ws), stream)
+        assert st == moe.MOE_OK
+        torch.cuda.synchronize()
+        assert torch.equal(h[:n_loc], res["h"][:n_loc]), call
+        assert torch.equal(y[:n_loc], res["y"][:n_loc]), call
+
+
 def test_fused_gemm_rejects_unsupported_shapes():
     w = SMALL[7]  # fp32
     x = torch.zeros((w.T, w.d), dtype=torch.float32, device="cuda")
