@@ -580,12 +580,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_lds_kernel(
   const int n_split = uniform(tm.classes) == 1 ? last : tall_last;  // last-round tiles split in two
   const bool split = total > 0 && n_split > 0 && last + n_split <= G;
   const bool narrow_last = N - (n_tiles - 1) * kOutCols <= kOutCols / 2;
-  // Pacing (blocked activation rows, forward only): the rows of a blocked copy
+  // Pacing (blocked activation rows): the rows of a blocked copy
   // arrive fast enough that the workgroups of one XCD drift apart by more k-steps
   // than its L2 holds, and re-fetch their round's shared rows and weight panels.
   // A workgroup that runs a tile ahead of most of its XCD waits at the tile
   // boundary. xcd_done holds one count per XCD, zeroed by the copy kernel.
-  const bool pace = AM == kABlocked && !SAVE && xcd_done != nullptr && (G & 7) == 0;
+  const bool pace = AM == kABlocked && xcd_done != nullptr && (G & 7) == 0;
   const int per_xcd = G >> 3;
   for (int i = 0;; ++i) {
     int tile, part = 0;  // part: 0 the whole tile, 1 or 2 its first or second half
@@ -624,7 +624,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_lds_kernel(
     const uint16_t* Bexp = B + static_cast<int64_t>(tc.e) * b_expert;
     // An expert with one row tile reads each weight panel once: stream it past the
     // caches, which then keep the rows and panels that are read again. (Measured:
-    // decode256's GEMM 6 % faster, ep8_share128's 2-4 %; on dense8, where four row
+    // decode256's GEMM 6 % faster, ep8_share128's 1-2 %; on dense8, where four row
     // tiles share each panel, the same policy was 6 % slower.)
     const bool stream = tc.mt_e == 1;
     if (half) {
@@ -713,7 +713,7 @@ hipError_t launch_grouped_gemm_lds(const void* a, const int32_t* perm, int64_t T
     if (gu != nullptr)
       hipLaunchKernelGGL((grouped_gemm_lds_kernel<true, kABlocked, true>), dim3(grid_gate_up), dim3(kThreads), 0,
                          stream, ab, wgu, hh, g, offsets, e_begin, e_loc, d, d_ff, 2 * d_ff, nm, nullptr, k, 0u,
-                         nullptr);
+                         xcd_done);
     else
       hipLaunchKernelGGL((grouped_gemm_lds_kernel<true, kABlocked, false>), dim3(grid_gate_up), dim3(kThreads), 0,
                          stream, ab, wgu, hh, nullptr, offsets, e_begin, e_loc, d, d_ff, 2 * d_ff, nm, nullptr, k, 0u,
