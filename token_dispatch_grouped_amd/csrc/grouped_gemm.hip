@@ -214,7 +214,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
 
 // ------------------------------------------------------------------ fp32 path
 
-constexpr int kFBM = 64, kFBN = 64, kFBK = 16;
+// K = 64 per stage, with every load of a stage issued before any is stored to
+// LDS: the small fp32 products are latency-bound, one memory round trip per stage
+// (T = 64 layer: GEMM 105 us with 16-wide stages loaded one element at a time,
+// 49 us so; issuing the next stage's loads before computing this one: 57 us).
+constexpr int kFBM = 64, kFBN = 64, kFBK = 64;
 
 template <bool SWIGLU>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_f32_kernel(
@@ -239,17 +243,26 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_f32_kernel(
     const float* Bexp = B + static_cast<int64_t>(tc.e) * b_expert;
     float g[4][4] = {}, u[4][4] = {};
     for (int k0 = 0; k0 < K; k0 += kFBK) {
-      for (int i = tid; i < kFBM * kFBK; i += kThreads) {
+      constexpr int kLoads = kFBM * kFBK / kThreads;  // per thread and operand
+      float av[kLoads], gv[kLoads], uv[kLoads];
+#pragma unroll
+      for (int q = 0; q < kLoads; ++q) {
+        const int i = q * kThreads + tid;
         const int r = i / kFBK, kk = i % kFBK;
         const int gr = min(row0 + r, row_end - 1);
-        As[kk][r] = (k0 + kk < K) ? A[static_cast<int64_t>(gr) * K + k0 + kk] : 0.f;
+        av[q] = (k0 + kk < K) ? A[static_cast<int64_t>(gr) * K + k0 + kk] : 0.f;
+        const int kb = i / kFBN, c = i % kFBN;
+        const bool ok = (k0 + kb < K) && (n0 + c < N);
+        const float* brow = Bexp + static_cast<int64_t>(k0 + kb) * ldb;
+        gv[q] = ok ? brow[n0 + c] : 0.f;
+        uv[q] = (SWIGLU && ok) ? brow[N + n0 + c] : 0.f;
       }
-      for (int i = tid; i < kFBK * kFBN; i += kThreads) {
-        const int kk = i / kFBN, c = i % kFBN;
-        const bool ok = (k0 + kk < K) && (n0 + c < N);
-        const float* brow = Bexp + static_cast<int64_t>(k0 + kk) * ldb;
-        Bg[kk][c] = ok ? brow[n0 + c] : 0.f;
-        if (SWIGLU) Bu[kk][c] = ok ? brow[N + n0 + c] : 0.f;
+#pragma unroll
+      for (int q = 0; q < kLoads; ++q) {
+        const int i = q * kThreads + tid;
+        As[i % kFBK][i / kFBK] = av[q];
+        Bg[i / kFBN][i % kFBN] = gv[q];
+        if (SWIGLU) Bu[i / kFBN][i % kFBN] = uv[q];
       }
       __syncthreads();
 #pragma unroll
