@@ -177,10 +177,14 @@ __device__ __forceinline__ void gemm_tile(uint16_t* smem, const uint16_t* __rest
     const int j = wave * L::B_PER_WAVE + jj;
     const int kl = RPI * j + lane / CPR;
     const int c = (lane % CPR) ^ (4 * (kl & 3));
-    int col;
-    if (SWIGLU) col = c < CPR / 2 ? n0 + 8 * c : N + n0 + 8 * (c - CPR / 2);
-    else col = n0 + 8 * c;
-    b_voff[jj] = (static_cast<uint32_t>(kl) * static_cast<uint32_t>(ldb) + static_cast<uint32_t>(col)) * 2u;
+    // 8 columns from n0 + 8 * (chunk within its half); past N they would be the
+    // next row's (or the up half's) first columns, so they point past the buffer
+    // and load zeros without a fetch (the last column block of N = 2880)
+    const int cc = SWIGLU && c >= CPR / 2 ? c - CPR / 2 : c;
+    const int col = (SWIGLU && c >= CPR / 2 ? N : 0) + n0 + 8 * cc;
+    b_voff[jj] = n0 + 8 * cc < N
+                     ? (static_cast<uint32_t>(kl) * static_cast<uint32_t>(ldb) + static_cast<uint32_t>(col)) * 2u
+                     : 0x80000000u;
   }
 
   // ---- fragment reads ----------------------------------------------------------------
